@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the fine-grained FP8 GEMM path on one MI355X.
+
+One step = the whole hot path over one batch: online 1x128 quantisation of the
+activations X, online 128x128 quantisation of the weight W, and the
+block-scaled FP8 GEMM with per-128-K-chunk FP32 promotion, Y = X W^T in bf16.
+Inputs are resident in HBM before timing starts; outputs are preallocated.
+
+Default workload: the large heavy-tail Fprop, X bf16 [16384, 7168] ~ Student-t(3),
+W bf16 [18432, 7168] ~ N(0, 0.02), Y bf16 [16384, 18432].
+
+Prints one JSON line: value = 2 M N K / step time (TFLOP/s including both
+quantisers), plus the GEMM kernel's roofline (HIP-event time of the kernel
+alone, on the stream it runs on) and the CPU oracle timed on a bounded sample
+of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s incl. quant (% of MFMA FP8 peak); quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+
+WORKLOADS = {
+    "large": ("large heavy-tail fprop", 16384, 18432, 7168),
+    "dense": ("dense fprop", 4096, 2048, 7168),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="large")
+    ap.add_argument("--kernel-reps", type=int, default=10, help="reps of each kernel timed alone")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample: rows of X")
+    ap.add_argument("--cpu-wrows", type=int, default=8192, help="oracle sample: rows of W")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its
+    readings give the factor between the counters and bytes moved."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "reps": 3}), flush=True)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the path is single-GPU; see the sharding notes in the design document).", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import fp8_fine_grained_fp8bq_amd as fb
+    import workloads
+
+    name, M, N, K = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    t0 = time.perf_counter()
+    cfg = workloads.large_fprop() if args.workload == "large" else workloads.dense_fprop()
+    log(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f}s")
+    x = torch.from_numpy(cfg.x.view(np.int16)).to(dev)
+    w = torch.from_numpy(cfg.w.view(np.int16)).to(dev)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)   # > 256 MB MALL
+    torch.cuda.synchronize()
+
+    def quant_x():
+        fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE, xq.data_ptr(), K, xs.data_ptr(), M, sp)
+
+    def quant_w():
+        fb.fp8bq_quant_w_128x128(w.data_ptr(), N, K, K, wq.data_ptr(), K, ws.data_ptr(), K // 128, None, N, sp)
+
+    def gemm():
+        fb.fp8bq_gemm(fb.FPROP, M, N, K, xq.data_ptr(), K, xs.data_ptr(), M, wq.data_ptr(), K,
+                      ws.data_ptr(), K // 128, y.data_ptr(), N, sp)
+
+    def step():
+        quant_x()
+        quant_w()
+        gemm()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), {value:.1f} TFLOP/s")
+
+    # each kernel alone; the quantisers after a 512 MB write that evicts the MALL
+    def time_kernel(fn, reps, cold):
+        durs = []
+        for _ in range(reps):
+            if cold:
+                flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            durs.append(a.elapsed_time(b) * 1e3)
+        return float(np.mean(durs)), float(np.median(durs))
+
+    tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
+    tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
+    tg, tg_med = time_kernel(gemm, args.kernel_reps, False)
+    bytes_qx = M * K * 3 + M * (K // 128) * 4
+    bytes_qw = N * K * 3 + (N // 128) * (K // 128) * 4
+    gemm_tflops = flops / (tg * 1e-6) / 1e12
+    log(f"[bench] quant X {tq_x:.1f} us ({bytes_qx / tq_x / 1e3:.0f} GB/s), quant W {tq_w:.1f} us "
+        f"({bytes_qw / tq_w / 1e3:.0f} GB/s), GEMM {tg:.1f} us ({gemm_tflops:.0f} TFLOP/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gemm as og
+        from oracle import quant as oq
+        r, nw = min(args.cpu_rows, M), min(args.cpu_wrows, N)
+        xs_h, ws_h = cfg.x[:r], cfg.w[:nw]
+        c0 = time.perf_counter()
+        q0, s0 = oq.quant_act_1x128(xs_h)
+        qw0, sw0 = oq.quant_w_128x128(ws_h)
+        og.fprop(q0, s0, qw0, sw0)
+        csec = time.perf_counter() - c0
+        cpu = {"value": 2.0 * r * nw * K / csec / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(),
+               "kind": "oracle",
+               "sample": f"quantise X[:{r}] (1x128) and W[:{nw}] (128x128), then the oracle GEMM of "
+                         f"those {r}x{nw}x{K} (fp64 chunk sums, fp32 promotion); {csec:.1f} s on the host"}
+        log(f"[bench] oracle sample: {csec:.1f} s -> {cpu['value'] * 1e3:.3f} GFLOP/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic: seeded Student-t(3) / N(0,1)+outliers activations, N(0,0.02) weights, bf16",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "act_tile": "1x128", "weight_block": "128x128",
+                   "fp8": "E4M3FN", "out": "bf16", "step": "quant_act + quant_w + gemm"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel<FPROP>", "avg_us": round(tg, 2), "median_us": round(tg_med, 2)},
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "frac_of_fp8_peak_incl_quant": round(value / PEAK_FP8_TFLOPS, 4),
+            "quant_act_us": round(tq_x, 2), "quant_act_GBps": round(bytes_qx / tq_x / 1e3, 1),
+            "quant_act_frac_hbm": round(bytes_qx / tq_x / 1e3 / PEAK_HBM_GBS, 4),
+            "quant_w_us": round(tq_w, 2), "quant_w_GBps": round(bytes_qw / tq_w / 1e3, 1),
+            "quant_w_frac_hbm": round(bytes_qw / tq_w / 1e3 / PEAK_HBM_GBS, 4),
+            "gemm_us": round(tg, 2), "gemm_TFLOPs": round(gemm_tflops, 1),
+            "quant_timing": "each kernel alone after a 512 MB write (MALL evicted), HIP events, mean",
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+"""fp8bq: fine-grained FP8 (E4M3, 1x128 / 128x128) quantisation and block-scaled
+FP8 GEMM for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in include/fp8bq.h (libfp8bq.so, built in
+this package directory by `build.py`). Every step of the computation runs in
+the library's HIP kernels; this module only marshals arguments. There is no
+fallback: if the library is missing or the device is not gfx950, calls raise.
+
+Two layers with the C names:
+
+* `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_gemm`,
+  `fp8bq_grouped_gemm`: pointer-level, exactly the C signatures (ints for
+  pointers and the stream); a non-zero status raises `Fp8bqError`.
+* `quant_act_1x128`, `quant_w_128x128`, `gemm`, `grouped_gemm`: take torch
+  tensors on the GPU, allocate the outputs with torch (memory and streams are
+  the only things torch provides) and call the same entry points on the
+  current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8bq.so")
+
+OK, E_INVAL, E_SHAPE, E_ALIGN, E_DEVICE, E_HIP = range(6)
+STATUS_NAMES = {0: "OK", 1: "E_INVAL", 2: "E_SHAPE", 3: "E_ALIGN", 4: "E_DEVICE", 5: "E_HIP"}
+FPROP, DGRAD, WGRAD = 0, 1, 2
+ACT_ROWWISE, ACT_COLWISE = 0, 1
+
+EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm",
+           "fp8bq_last_error", "fp8bq_version")
+
+
+class Fp8bqError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp8bq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fp8_fine_grained_fp8bq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, fp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+        L.fp8bq_quant_act_1x128.argtypes = [vp, i64, i64, i64, i32, vp, i64, fp, i64, vp]
+        L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, vp]
+        L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
+        L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
+                                         vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
+        for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm"):
+            getattr(L, f).restype = ctypes.c_int
+        L.fp8bq_last_error.restype = ctypes.c_char_p
+        L.fp8bq_last_error.argtypes = []
+        L.fp8bq_version.restype = ctypes.c_char_p
+        L.fp8bq_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> int:
+    if status != OK:
+        raise Fp8bqError(fn, status, lib().fp8bq_last_error().decode())
+    return status
+
+
+# ---------------------------------------------------------------------------
+# pointer-level entry points (C names)
+# ---------------------------------------------------------------------------
+
+def fp8bq_quant_act_1x128(x, rows, cols, ldx, mode, q, ldq, s, lds, stream=0):
+    return _check("fp8bq_quant_act_1x128",
+                  lib().fp8bq_quant_act_1x128(x, rows, cols, ldx, mode, q, ldq, s, lds, stream))
+
+
+def fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, stream=0):
+    return _check("fp8bq_quant_w_128x128",
+                  lib().fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, stream))
+
+
+def fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
+    return _check("fp8bq_gemm",
+                  lib().fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream))
+
+
+def fp8bq_grouped_gemm(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
+    """`row_off` is a sequence of groups + 1 ints (host memory)."""
+    arr = (ctypes.c_int64 * (groups + 1))(*[int(v) for v in row_off]) if row_off is not None else None
+    return _check("fp8bq_grouped_gemm",
+                  lib().fp8bq_grouped_gemm(groups, arr, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb,
+                                           out, ldo, stream))
+
+
+def version() -> str:
+    return lib().fp8bq_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor convenience layer (allocation + marshalling only)
+# ---------------------------------------------------------------------------
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _bf16_2d(t, name):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major bf16 tensor (got {t.dtype}, {tuple(t.shape)})")
+    return t
+
+
+def quant_act_1x128(x, mode: int = ACT_ROWWISE):
+    """x bf16 [rows, cols] -> (q uint8, s float32) as laid out by the C ABI:
+    ROWWISE q [rows, cols], s [cols/128, rows]; COLWISE q [cols, rows], s [rows/128, cols]."""
+    import torch
+    _bf16_2d(x, "x")
+    rows, cols = x.shape
+    if mode == ACT_ROWWISE:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        s = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+        ldq, lds = cols, rows
+    else:
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows // 128, cols), dtype=torch.float32, device=x.device)
+        ldq, lds = rows, cols
+    fp8bq_quant_act_1x128(x.data_ptr(), rows, cols, x.stride(0), mode, q.data_ptr(), ldq,
+                          s.data_ptr(), lds, _stream(x))
+    return q, s
+
+
+def quant_w_128x128(w, transposed_copy: bool = False):
+    """w bf16 [n, k] -> (q uint8 [n, k], s float32 [n/128, k/128], qt uint8 [k, n] or None)."""
+    import torch
+    _bf16_2d(w, "w")
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    s = torch.empty((n // 128, k // 128), dtype=torch.float32, device=w.device)
+    qt = torch.empty((k, n), dtype=torch.uint8, device=w.device) if transposed_copy else None
+    fp8bq_quant_w_128x128(w.data_ptr(), n, k, w.stride(0), q.data_ptr(), k, s.data_ptr(), k // 128,
+                          qt.data_ptr() if qt is not None else None, n, _stream(w))
+    return q, s, qt
+
+
+def gemm(op: int, a, sa, b, sb, out=None):
+    """a uint8 [m, k] with chunk-major scales sa [k/128, >=m]; b uint8 [n, k] with
+    sb laid out per `op` (see include/fp8bq.h). Returns out (bf16 or fp32) [m, n]."""
+    import torch
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        dt = torch.float32 if op == WGRAD else torch.bfloat16
+        out = torch.empty((m, n), dtype=dt, device=a.device)
+    fp8bq_gemm(op, m, n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
+               b.data_ptr(), b.stride(0), sb.data_ptr(), sb.stride(0), out.data_ptr(), out.stride(0),
+               _stream(a))
+    return out
+
+
+def grouped_gemm(row_off, a, sa, b, sb, out=None):
+    """row_off: host sequence of G + 1 row offsets (multiples of 128); a uint8 [m, k];
+    sa [k/128, >=m]; b uint8 [G, n, k]; sb float32 [G, n/128, k/128]. Returns bf16 [m, n]."""
+    import torch
+    G, n, k = b.shape
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    fp8bq_grouped_gemm(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
+                       b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
+                       out.stride(0), _stream(a))
+    return out

@@ -1,0 +1,183 @@
+// C-ABI entry points of libfp8bq: argument validation (host only, before any
+// HIP call), the device check, and dispatch to the kernel launchers.
+// The operations and their layouts are specified in include/fp8bq.h.
+#include "../../include/fp8bq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+// Current device must exist and be gfx950. The arch lookup is cached per device.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(FP8BQ_E_DEVICE, "no HIP device available");
+  }
+  if (dev >= kMaxDevices) return fail(FP8BQ_E_DEVICE, "device index %d out of range", dev);
+  int st = g_arch[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FP8BQ_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_release);
+    if (st == 2) return fail(FP8BQ_E_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (st != 1) return fail(FP8BQ_E_DEVICE, "device %d is not gfx950", dev);
+  return FP8BQ_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP8BQ_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return FP8BQ_OK;
+}
+
+constexpr int64_t kMaxTiles = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bq_last_error(void) { return g_err; }
+
+const char* fp8bq_version(void) { return "fp8bq 0.1 (gfx950)"; }
+
+int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                          void* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+  if (!x || !q || !s) return fail(FP8BQ_E_INVAL, "quant_act: null pointer");
+  if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "quant_act: rows and cols must be positive");
+  if (mode != FP8BQ_ACT_ROWWISE && mode != FP8BQ_ACT_COLWISE)
+    return fail(FP8BQ_E_INVAL, "quant_act: mode must be ROWWISE (0) or COLWISE (1), got %d", mode);
+  if (ldx < cols) return fail(FP8BQ_E_INVAL, "quant_act: ldx (%lld) < cols (%lld)", (long long)ldx, (long long)cols);
+  if (cols % 128) return fail(FP8BQ_E_SHAPE, "quant_act: cols (%lld) must be a multiple of 128", (long long)cols);
+  if (mode == FP8BQ_ACT_ROWWISE) {
+    if (ldq < cols) return fail(FP8BQ_E_INVAL, "quant_act: ldq < cols");
+    if (lds < rows) return fail(FP8BQ_E_INVAL, "quant_act: lds < rows");
+    if (rows * (cols / 128) >= kMaxTiles) return fail(FP8BQ_E_SHAPE, "quant_act: too many tiles");
+  } else {
+    if (rows % 128) return fail(FP8BQ_E_SHAPE, "quant_act: column-wise mode needs rows (%lld) to be a multiple of 128", (long long)rows);
+    if (ldq < rows) return fail(FP8BQ_E_INVAL, "quant_act: ldq < rows (transposed output)");
+    if (lds < cols) return fail(FP8BQ_E_INVAL, "quant_act: lds < cols");
+    if (rows / 128 > 65535 || cols / 64 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
+  }
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))
+    return fail(FP8BQ_E_ALIGN, "quant_act: x and q must be 16-byte aligned, s 4-byte aligned");
+  if (ldx % 8 || ldq % 16) return fail(FP8BQ_E_ALIGN, "quant_act: ldx must be a multiple of 8 and ldq of 16");
+  if (int st = check_device()) return st;
+  hipStream_t str = reinterpret_cast<hipStream_t>(stream);
+  if (mode == FP8BQ_ACT_ROWWISE)
+    return launched(fp8bq::launch_quant_act_rows(static_cast<const uint16_t*>(x), rows, cols, ldx,
+                                                 static_cast<uint8_t*>(q), ldq, s, lds, str), "quant_act");
+  return launched(fp8bq::launch_quant_act_cols(static_cast<const uint16_t*>(x), rows, cols, ldx,
+                                               static_cast<uint8_t*>(q), ldq, s, lds, str), "quant_act");
+}
+
+int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
+                          float* s, int64_t lds, void* qt, int64_t ldqt, void* stream) {
+  if (!w || !q || !s) return fail(FP8BQ_E_INVAL, "quant_w: null pointer");
+  if (n <= 0 || k <= 0) return fail(FP8BQ_E_INVAL, "quant_w: n and k must be positive");
+  if (ldw < k || ldq < k) return fail(FP8BQ_E_INVAL, "quant_w: ldw and ldq must be >= k");
+  if (lds < k / 128) return fail(FP8BQ_E_INVAL, "quant_w: lds must be >= k / 128");
+  if (qt && ldqt < n) return fail(FP8BQ_E_INVAL, "quant_w: ldqt must be >= n");
+  if (n % 128 || k % 128) return fail(FP8BQ_E_SHAPE, "quant_w: n (%lld) and k (%lld) must be multiples of 128", (long long)n, (long long)k);
+  if (n / 128 > 65535 || k / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "quant_w: too large");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4) || (qt && !aligned(qt, 16)))
+    return fail(FP8BQ_E_ALIGN, "quant_w: w, q, qt must be 16-byte aligned, s 4-byte aligned");
+  if (ldw % 8 || ldq % 16 || (qt && ldqt % 16))
+    return fail(FP8BQ_E_ALIGN, "quant_w: ldw must be a multiple of 8, ldq and ldqt of 16");
+  if (int st = check_device()) return st;
+  return launched(fp8bq::launch_quant_w(static_cast<const uint16_t*>(w), n, k, ldw, static_cast<uint8_t*>(q),
+                                        ldq, s, lds, static_cast<uint8_t*>(qt), ldqt,
+                                        reinterpret_cast<hipStream_t>(stream)), "quant_w");
+}
+
+namespace {
+
+int check_gemm_common(const char* who, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                      const float* sa, const void* b, int64_t ldb, const float* sb, const void* out,
+                      int64_t ldo, int out_elem_bytes) {
+  if (!a || !b || !sa || !sb || !out) return fail(FP8BQ_E_INVAL, "%s: null pointer", who);
+  if (m <= 0 || n <= 0 || k <= 0) return fail(FP8BQ_E_INVAL, "%s: m, n, k must be positive", who);
+  if (lda < k || ldb < k) return fail(FP8BQ_E_INVAL, "%s: lda and ldb must be >= k", who);
+  if (ldo < n) return fail(FP8BQ_E_INVAL, "%s: ldo must be >= n", who);
+  if (k % 128 || n % 128) return fail(FP8BQ_E_SHAPE, "%s: k (%lld) and n (%lld) must be multiples of 128", who, (long long)k, (long long)n);
+  if (((m + 255) / 256) * ((n + 255) / 256) >= kMaxTiles) return fail(FP8BQ_E_SHAPE, "%s: too many tiles", who);
+  if (lda >= ((int64_t)1 << 23) || ldb >= ((int64_t)1 << 23))
+    return fail(FP8BQ_E_SHAPE, "%s: lda and ldb must be below 2^23 (256 rows within 2 GiB)", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(sa, 4) || !aligned(sb, 4))
+    return fail(FP8BQ_E_ALIGN, "%s: a, b, out must be 16-byte aligned, scales 4-byte aligned", who);
+  if (lda % 16 || ldb % 16 || (ldo * out_elem_bytes) % 16)
+    return fail(FP8BQ_E_ALIGN, "%s: lda, ldb must be multiples of 16 and ldo*sizeof(out) of 16 bytes", who);
+  return FP8BQ_OK;
+}
+
+}  // namespace
+
+int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* sa,
+               int64_t ldsa, const void* b, int64_t ldb, const float* sb, int64_t ldsb, void* out,
+               int64_t ldo, void* stream) {
+  if (op != FP8BQ_FPROP && op != FP8BQ_DGRAD && op != FP8BQ_WGRAD)
+    return fail(FP8BQ_E_INVAL, "gemm: op must be FPROP (0), DGRAD (1) or WGRAD (2), got %d", op);
+  if (int st = check_gemm_common("gemm", m, n, k, a, lda, sa, b, ldb, sb, out, ldo, op == FP8BQ_WGRAD ? 4 : 2))
+    return st;
+  if (ldsa < m) return fail(FP8BQ_E_INVAL, "gemm: ldsa must be >= m");
+  if (op == FP8BQ_FPROP && ldsb < k / 128) return fail(FP8BQ_E_INVAL, "gemm: FPROP ldsb must be >= k / 128");
+  if (op == FP8BQ_DGRAD && ldsb < n / 128) return fail(FP8BQ_E_INVAL, "gemm: DGRAD ldsb must be >= n / 128");
+  if (op == FP8BQ_WGRAD && ldsb < n) return fail(FP8BQ_E_INVAL, "gemm: WGRAD ldsb must be >= n");
+  if (int st = check_device()) return st;
+  return launched(fp8bq::launch_gemm(op, m, n, k, static_cast<const uint8_t*>(a), lda, sa, ldsa,
+                                     static_cast<const uint8_t*>(b), ldb, sb, ldsb, out, ldo,
+                                     reinterpret_cast<hipStream_t>(stream)), "gemm");
+}
+
+int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
+                       int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
+                       const float* sb, int64_t ldsb, void* out, int64_t ldo, void* stream) {
+  if (groups < 1 || groups > fp8bq::kMaxGroups)
+    return fail(FP8BQ_E_INVAL, "grouped_gemm: groups must be in [1, %d], got %d", fp8bq::kMaxGroups, groups);
+  if (!row_off) return fail(FP8BQ_E_INVAL, "grouped_gemm: null row_off");
+  if (row_off[0] != 0) return fail(FP8BQ_E_SHAPE, "grouped_gemm: row_off[0] must be 0");
+  for (int e = 0; e < groups; ++e) {
+    if (row_off[e + 1] < row_off[e]) return fail(FP8BQ_E_SHAPE, "grouped_gemm: row_off must be non-decreasing (at %d)", e);
+    if (row_off[e + 1] % 128) return fail(FP8BQ_E_SHAPE, "grouped_gemm: row_off[%d] = %lld is not a multiple of 128", e + 1, (long long)row_off[e + 1]);
+  }
+  const int64_t m = row_off[groups];
+  if (m / 128 >= ((int64_t)1 << 30)) return fail(FP8BQ_E_SHAPE, "grouped_gemm: too many rows");
+  if (int st = check_gemm_common("grouped_gemm", m > 0 ? m : 1, n, k, a, lda, sa, b, ldb, sb, out, ldo, 2))
+    return st;
+  if (ldsa < m) return fail(FP8BQ_E_INVAL, "grouped_gemm: ldsa must be >= m");
+  if (ldsb < k / 128) return fail(FP8BQ_E_INVAL, "grouped_gemm: ldsb must be >= k / 128");
+  if (int st = check_device()) return st;
+  if (m == 0) return FP8BQ_OK;
+  return launched(fp8bq::launch_grouped_gemm(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda, sa, ldsa,
+                                             static_cast<const uint8_t*>(b), ldb, sb, ldsb,
+                                             static_cast<uint16_t*>(out), ldo, reinterpret_cast<hipStream_t>(stream)),
+                  "grouped_gemm");
+}
+
+}  // extern "C"

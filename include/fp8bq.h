@@ -1,0 +1,170 @@
+/*
+ * fp8bq -- fine-grained FP8 (E4M3) quantisation and block-scaled FP8 GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the FP8 mixed-precision Linear of the DeepSeek-V3 report
+ * (Chinese translation, chapter 3 "Infrastructure"):
+ *   - section 3.3.2 "fine-grained quantization" and Figure 7a: activations are
+ *     scaled per 1x128 tile (one token, 128 channels), weights per 128x128
+ *     block; the scales run along the GEMM's inner dimension K;
+ *   - section 3.3.2 "online quantization": the max-abs of every tile / block is
+ *     taken on the fly, the scale is derived from it and the data is cast to
+ *     FP8 at once (the tech note "DeepSeek-V3 FP8 dynamic quantisation" gives
+ *     s = absmax / F_max and q = round(x / s));
+ *   - section 3.3.2 "mantissa over exponents": E4M3 for every tensor;
+ *   - section 3.3.2 "increasing accumulation precision" and Figure 7b: the
+ *     partial sum of every N_C = 128 K-elements is promoted to an FP32
+ *     accumulator, where it is multiplied by both operands' scales;
+ *   - section 3.3.1 and Figure 6: Fprop, Dgrad and Wgrad all run in FP8 and
+ *     produce BF16 or FP32;
+ *   - section 3.3.3 "low-precision activations" / 3.5.2 "transposed GEMM":
+ *     the weight-gradient GEMM needs the tiles along the token dimension
+ *     (128x1);
+ *   - section 3.3.3 "low-precision communication": the MoE up-projection runs
+ *     an FP8 Fprop per expert.
+ *
+ * Numerics (the same on every entry point):
+ *   FP8 is OCP E4M3FN (largest finite 448, no infinities, 0x7F/0xFF NaN).
+ *   s = fl32(absmax / 448) (IEEE binary32 quotient, round-to-nearest-even);
+ *   q = E4M3 round-to-nearest-even of fl32(x / s), saturating to +-448, sign
+ *   kept for zeros; a tile whose absmax is 0 gets s = 0 and codes +0 / -0.
+ *   Inputs must be finite (NaN / Inf give unspecified codes and outputs).
+ *
+ * Conventions:
+ *   - All matrices are row-major with an explicit leading dimension (ld, in
+ *     elements). bf16 data is passed as raw 16-bit patterns.
+ *   - Every pointer except `row_off` of fp8bq_grouped_gemm is a DEVICE pointer
+ *     owned by the caller. The library never allocates or frees memory and
+ *     keeps no device state; outputs must not alias inputs.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work and return; results are ready when the stream has run it.
+ *   - Arguments are validated on the host before any GPU call. The return
+ *     value is an fp8bq_status; on any status other than FP8BQ_OK nothing was
+ *     enqueued and fp8bq_last_error() (thread-local) describes the problem.
+ *   - Alignment: data pointers 16-byte aligned; bf16 leading dimensions
+ *     multiples of 8, FP8 leading dimensions multiples of 16, float scale
+ *     pointers 4-byte aligned.
+ */
+#ifndef FP8BQ_H
+#define FP8BQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BQ_OK = 0,
+  FP8BQ_E_INVAL = 1,   /* null pointer, non-positive size, ld too small, bad enum */
+  FP8BQ_E_SHAPE = 2,   /* a dimension is not a multiple of 128 where required, bad group offsets */
+  FP8BQ_E_ALIGN = 3,   /* pointer or leading dimension misaligned */
+  FP8BQ_E_DEVICE = 4,  /* no HIP device, or the current device is not gfx950 */
+  FP8BQ_E_HIP = 5      /* the HIP runtime reported an error when launching */
+} fp8bq_status;
+
+typedef enum {
+  FP8BQ_FPROP = 0,     /* Y = X W^T : B block-scaled [N/128][K/128], bf16 out   */
+  FP8BQ_DGRAD = 1,     /* dX = dY W : B = W^T, scales = W's grid,   bf16 out    */
+  FP8BQ_WGRAD = 2      /* dW = dY^T X : B row-scaled [K/128][N],    fp32 out    */
+} fp8bq_op;
+
+enum { FP8BQ_ACT_ROWWISE = 0, FP8BQ_ACT_COLWISE = 1 };
+
+/*
+ * Online activation quantisation (report section 3.3.2, Figure 7a; for the
+ * column-wise mode section 3.3.3 "low-precision activations" and 3.5.2).
+ *
+ * x      bf16 [rows, cols], leading dimension ldx >= cols.
+ * mode   FP8BQ_ACT_ROWWISE: 1x128 tiles along each row (cols % 128 == 0).
+ *          q  E4M3 [rows, cols], ldq >= cols.
+ *          s  float, tile (r, c) -- row r, columns [128c, 128c+128) -- at
+ *             s[c * lds + r], lds >= rows ("chunk-major").
+ *        FP8BQ_ACT_COLWISE: 128x1 tiles along each column (rows % 128 == 0,
+ *          cols % 128 == 0); the result is written transposed so that the
+ *          grouped (token) dimension is contiguous:
+ *          q  E4M3 [cols, rows], ldq >= rows; q[j * ldq + r] encodes x[r][j].
+ *          s  tile (rows [128c, 128c+128), column j) at s[c * lds + j],
+ *             lds >= cols.
+ * Errors: E_INVAL (null, rows/cols <= 0, ld too small, bad mode), E_SHAPE,
+ *         E_ALIGN, E_DEVICE, E_HIP.
+ */
+int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+                          void* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/*
+ * Online weight quantisation with 128x128 blocks (report section 3.3.2,
+ * Figure 7a: per 128 input channels x 128 output channels).
+ *
+ * w      bf16 [n, k], ldw >= k; n % 128 == 0 and k % 128 == 0.
+ * q      E4M3 [n, k], ldq >= k.
+ * s      float block grid: block (nb, kb) at s[nb * lds + kb], lds >= k/128.
+ * qt     optional (may be NULL): the transposed FP8 copy [k, n], ldqt >= n,
+ *        qt[j * ldqt + i] == q[i * ldq + j]. It is the B operand of the Dgrad
+ *        GEMM (block quantisation commutes with transposition).
+ * Errors: as above.
+ */
+int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
+                          void* q, int64_t ldq, float* s, int64_t lds,
+                          void* qt, int64_t ldqt, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM with per-128-K-chunk promotion (report section 3.3.2
+ * "increasing accumulation precision", Figure 7b; section 3.3.1, Figure 6):
+ *
+ *   out[i][j] = sum_c ( sum_{k in chunk c} dec(a[i][k]) * dec(b[j][k]) ) * sa(i,c) * sb(j,c)
+ *
+ * accumulated in FP32; each chunk is 128 consecutive k. Both operands are
+ * stored with k contiguous ("TN"): a E4M3 [m, k] (lda >= k), b E4M3 [n, k]
+ * (ldb >= k). k % 128 == 0 and n % 128 == 0; m >= 1 is free.
+ *
+ * sa     row scales of a, chunk-major: sa(i, c) = sa[c * ldsa + i], ldsa >= m
+ *        (the layout fp8bq_quant_act_1x128 writes).
+ * sb     op FPROP: block grid of the weight b: sb(j, c) = sb[(j/128) * ldsb + c],
+ *                  ldsb >= k/128 (the layout fp8bq_quant_w_128x128 writes).
+ *        op DGRAD: b is the transposed copy qt of a weight W [k, n] and sb is
+ *                  W's own block grid: sb(j, c) = sb[c * ldsb + j/128],
+ *                  ldsb >= n/128.
+ *        op WGRAD: row scales of b, chunk-major: sb(j, c) = sb[c * ldsb + j],
+ *                  ldsb >= n (column-wise activation quantisation output).
+ * out    FPROP / DGRAD: bf16 [m, n] (round-to-nearest-even), ldo >= n.
+ *        WGRAD: float [m, n], ldo >= n.
+ * Errors: as above.
+ */
+int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k,
+               const void* a, int64_t lda, const float* sa, int64_t ldsa,
+               const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+               void* out, int64_t ldo, void* stream);
+
+/*
+ * Grouped (per-expert) Fprop for the MoE up-projection (report section 3.3.3
+ * "low-precision communication": FP8 Fprop of the dispatched activations).
+ *
+ * groups   G >= 1 experts, G <= 1024.
+ * row_off  HOST array of G + 1 int64: expert e owns rows [row_off[e],
+ *          row_off[e+1]) of a and out; row_off[0] == 0, non-decreasing, every
+ *          entry a multiple of 128 (pad each expert's rows, e.g. with zeros).
+ *          m = row_off[G].
+ * a, sa    E4M3 [m, k] with chunk-major row scales (as fp8bq_gemm), ldsa >= m.
+ * b        G weights of [n, k] each, row stride ldb, expert e's at b + e*n*ldb.
+ * sb       G block grids [n/128][k/128], row stride ldsb, expert e's at
+ *          sb + e*(n/128)*ldsb.
+ * out      bf16 [m, n], ldo >= n.
+ * Errors: as above; E_SHAPE for bad offsets.
+ */
+int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                       const void* a, int64_t lda, const float* sa, int64_t ldsa,
+                       const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                       void* out, int64_t ldo, void* stream);
+
+/* Thread-local description of the last non-OK status on this thread. */
+const char* fp8bq_last_error(void);
+
+/* Library version string. */
+const char* fp8bq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BQ_H */

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+making any HIP call. Valid arguments on a machine without a GPU give
+FP8BQ_E_DEVICE (only run where no device is visible, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_fine_grained_fp8bq_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bq.h")
+
+A16 = 0x10000          # stand-in "device addresses": 16-byte aligned, never dereferenced
+B16 = 0x20000
+S4 = 0x30000
+O16 = 0x40000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fb.LIB_PATH):
+        pytest.skip("libfp8bq.so not built (run __graft_entry__.build())")
+    return fb.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8bq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm",
+                 "fp8bq_last_error"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert set(_declared()) <= set(fb.EXPORTS)
+    assert L.fp8bq_version().decode().startswith("fp8bq")
+
+
+def _st(L, fn, *args):
+    return getattr(L, fn)(*args)
+
+
+def test_quant_act_validation(L):
+    f = "fp8bq_quant_act_1x128"
+    ok = [A16, 256, 1024, 1024, 0, B16, 1024, S4, 256, None]
+    assert _st(L, f, *[None] + ok[1:]) == fb.E_INVAL
+    assert _st(L, f, *ok[:1] + [0] + ok[2:]) == fb.E_INVAL                      # rows
+    assert _st(L, f, *ok[:4] + [2] + ok[5:]) == fb.E_INVAL                      # mode
+    assert _st(L, f, *ok[:3] + [1000] + ok[4:]) == fb.E_INVAL                   # ldx < cols
+    assert _st(L, f, *ok[:2] + [1000, 1000] + ok[4:6] + [1000] + ok[7:]) == fb.E_SHAPE
+    assert _st(L, f, *ok[:8] + [255, None]) == fb.E_INVAL                       # lds < rows
+    assert _st(L, f, *[A16 + 2] + ok[1:]) == fb.E_ALIGN
+    assert _st(L, f, *ok[:3] + [1028] + ok[4:]) == fb.E_ALIGN                   # ldx % 8
+    col = [A16, 200, 1024, 1024, 1, B16, 256, S4, 1024, None]
+    assert _st(L, f, *col) == fb.E_SHAPE                                        # rows % 128 (col-wise)
+    col[1] = 256
+    col[6] = 200
+    assert _st(L, f, *col) == fb.E_INVAL                                        # ldq < rows
+    assert "ldq" in L.fp8bq_last_error().decode()
+
+
+def test_quant_w_validation(L):
+    f = "fp8bq_quant_w_128x128"
+    ok = [A16, 256, 384, 384, B16, 384, S4, 3, O16, 256, None]
+    assert _st(L, f, *[A16, 0] + ok[2:]) == fb.E_INVAL
+    assert _st(L, f, *ok[:1] + [200, 384, 384] + ok[4:]) == fb.E_SHAPE
+    assert _st(L, f, *ok[:7] + [2] + ok[8:]) == fb.E_INVAL                      # lds < k/128
+    assert _st(L, f, *ok[:9] + [128, None]) == fb.E_INVAL                       # ldqt < n
+    assert _st(L, f, *ok[:8] + [O16 + 1, 256, None]) == fb.E_ALIGN
+    assert _st(L, f, *ok[:4] + [B16 + 8] + ok[5:]) == fb.E_ALIGN
+
+
+def _gemm_ok(op=0):
+    # m, n, k = 300, 384, 1024
+    ldsb = {0: 8, 1: 3, 2: 384}[op]
+    return [op, 300, 384, 1024, A16, 1024, S4, 300, B16, 1024, S4, ldsb, O16, 384, None]
+
+
+def test_gemm_validation(L):
+    f = "fp8bq_gemm"
+    for op in (0, 1, 2):
+        ok = _gemm_ok(op)
+        bad = list(ok); bad[0] = 3
+        assert _st(L, f, *bad) == fb.E_INVAL
+        bad = list(ok); bad[4] = None
+        assert _st(L, f, *bad) == fb.E_INVAL
+        bad = list(ok); bad[3] = 1000; bad[5] = 1008; bad[9] = 1008
+        assert _st(L, f, *bad) == fb.E_SHAPE                                   # k % 128
+        bad = list(ok); bad[2] = 200; bad[13] = 208
+        assert _st(L, f, *bad) == fb.E_SHAPE                                   # n % 128
+        bad = list(ok); bad[7] = 299
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # ldsa < m
+        bad = list(ok); bad[11] = ok[11] - 1
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # ldsb
+        bad = list(ok); bad[5] = 1032
+        assert _st(L, f, *bad) == fb.E_ALIGN                                   # lda % 16
+        bad = list(ok); bad[12] = O16 + 8
+        assert _st(L, f, *bad) == fb.E_ALIGN
+        bad = list(ok); bad[13] = 383
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # ldo < n
+
+
+def test_grouped_validation(L):
+    f = "fp8bq_grouped_gemm"
+    P = ctypes.POINTER(ctypes.c_int64)
+
+    def off(*v):
+        return (ctypes.c_int64 * len(v))(*v)
+    base = [None, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56, O16, 2048, None]
+    assert _st(L, f, 0, off(0), *base[1:]) == fb.E_INVAL
+    assert _st(L, f, 257, off(*([0] * 258)), *base[1:]) == fb.E_INVAL
+    assert _st(L, f, 2, None, *base[1:]) == fb.E_INVAL
+    assert _st(L, f, 2, off(128, 256, 512), *base[1:]) == fb.E_SHAPE          # row_off[0] != 0
+    assert _st(L, f, 2, off(0, 256, 128), *base[1:]) == fb.E_SHAPE            # decreasing
+    assert _st(L, f, 2, off(0, 100, 512), *base[1:]) == fb.E_SHAPE            # not multiple of 128
+    bad = list(base); bad[6] = 500
+    assert _st(L, f, 2, off(0, 256, 512), *bad[1:]) == fb.E_INVAL             # ldsa < m
+    bad = list(base); bad[10] = 55
+    assert _st(L, f, 2, off(0, 256, 512), *bad[1:]) == fb.E_INVAL             # ldsb < k/128
+    assert isinstance(P, type)
+
+
+def test_binding_raises_with_message(L):
+    with pytest.raises(fb.Fp8bqError) as ei:
+        fb.fp8bq_gemm(7, 1, 128, 128, A16, 128, S4, 1, B16, 128, S4, 1, O16, 128, 0)
+    assert ei.value.status == fb.E_INVAL and "op" in str(ei.value)
+
+
+def _no_device():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_device(), reason="a GPU is visible; valid arguments would launch")
+def test_valid_arguments_without_device_report_e_device(L):
+    assert _st(L, "fp8bq_gemm", *_gemm_ok(0)) == fb.E_DEVICE
+    assert _st(L, "fp8bq_quant_act_1x128", A16, 256, 1024, 1024, 0, B16, 1024, S4, 256, None) == fb.E_DEVICE
+    assert _st(L, "fp8bq_quant_w_128x128", A16, 256, 384, 384, B16, 384, S4, 3, None, 0, None) == fb.E_DEVICE
+    off = (ctypes.c_int64 * 3)(0, 256, 512)
+    assert _st(L, "fp8bq_grouped_gemm", 2, off, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56,
+               O16, 2048, None) == fb.E_DEVICE
+    assert "device" in L.fp8bq_last_error().decode()
