@@ -20,13 +20,18 @@
 //    second, so a lane's four result registers are four consecutive output
 //    columns j of one output row i: one activation scale per (lane, 16-row
 //    subtile) per chunk and 8-byte (bf16) / 16-byte (fp32) output stores.
-//  * Workgroup tile 256 x 256, 8 waves (2 per SIMD) of 64 (i) x 128 (j):
-//    128 accumulator VGPRs per lane, 32 MFMAs per wave per chunk.
+//  * Workgroup tile 256 x 256, 8 waves (two per SIMD) of 64 x 128: 128
+//    accumulator VGPRs per lane (the promotion FMAs need the accumulator in the
+//    256 VGPRs the VALU can address, which rules out 128 x 128 wave tiles),
+//    24 KB of LDS operand reads per wave per chunk.
 //  * Operands stream global -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging), two 66 KB stages (A 32 KB, B 32 KB, scales 2 KB), one barrier
 //    per chunk; the next chunk's loads run under the current chunk's MFMAs.
-//  * LDS rows are 128 bytes (one chunk); the 16-byte slots of row r are
-//    XOR-swizzled by (r & 7) so the MFMA operand reads spread over the banks.
+//  * LDS rows are 128 bytes (one chunk); the 16-byte slot s of row r is stored
+//    at slot s ^ (r & 7) ^ ((r >> 3) & 1). An operand read has 16 lanes on 16
+//    consecutive rows at one logical slot; measured on gfx950, ds_read_b128
+//    runs at full LDS bandwidth only if rows r and r + 8 also land in different
+//    slots (an (r & 7) swizzle alone halves it).
 //  * Workgroups are remapped so that each XCD (own L2) gets a contiguous range
 //    of output tiles, walked in groups of 8 row-tiles: the blocks resident on
 //    one XCD share activation and weight panels in its L2.
@@ -39,12 +44,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kThreads = 512;
-constexpr int kWavesM = 4, kWavesN = 2;
-constexpr int WM = BM / kWavesM;   // 64
-constexpr int WN = BN / kWavesN;   // 128
-constexpr int TM = WM / 16;        // 4
-constexpr int TN = WN / 16;        // 8
 constexpr int kABytes = BM * BK;
 constexpr int kBBytes = BN * BK;
 constexpr int kSaOff = kABytes + kBBytes;
@@ -53,8 +52,20 @@ constexpr int kStage = kSbOff + BN * 4;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-static_assert(kWavesM * kWavesN * 64 == kThreads, "wave grid");
-static_assert(WN == 128, "one weight block column per wave");
+template <int WAVES_M, int WAVES_N>
+struct Cfg {
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WM = BM / WAVES_M;
+  static constexpr int WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16;
+  static constexpr int TN = WN / 16;
+  static constexpr int kRowsPerRound = 8 * kWaves;        // one dwordx4 DMA per wave covers 8 rows
+  static constexpr int kRounds = BM / kRowsPerRound;
+  static_assert(WN == 128, "one weight block column per wave");
+  static_assert(BM == BN && BM % kRowsPerRound == 0, "tile / wave grid");
+  static_assert(kWaves == 4 || kWaves == 8, "scale loaders: four 64-lane dword DMAs per side");
+};
 
 struct GemmArgs {
   int64_t m, n, k;
@@ -81,9 +92,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // M0 is reserved by the compiler; on gfx950 only LDS DMA reads it and the
-// compiler itself never keeps a value there across these statements.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// compiler itself never keeps a value there across these statements (the
+// build passes -Wno-inline-asm for this clobber).
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
@@ -92,7 +102,6 @@ __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
-#pragma clang diagnostic pop
 
 // Tile position: logical tile index after the XCD remap and the grouped walk.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -110,70 +119,106 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsize;
 }
 
-// One K-chunk of the wave's 64 x 128 tile from one LDS stage: per 16x16 subtile
-// one MFMA (fresh partial sum of the chunk) and four FMAs folding it into the
-// FP32 accumulator. The two waves sharing a SIMD overlap one's MFMAs with the
-// other's FMAs.
-template <int KIND>
-__device__ __forceinline__ void compute_chunk(const uint8_t* __restrict__ As, v4f (&acc)[TM][TN],
-                                              int wave_m, int wave_n, int l16, int lq, int off0,
-                                              int off1) {
+// Physical-slot XOR of LDS row r (see the layout note at the top).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ v8i frag(const uint8_t* rowp, int off0, int off1) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + off0);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(rowp + off1);
+  return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+// Per-chunk promotion state carried across the barrier: the last weight
+// subtile's MFMA results of a chunk are folded at the start of the next chunk,
+// after the barrier, so those MFMAs keep the matrix core busy while the waves
+// synchronise.
+template <int KIND, class C>
+struct Carry {
+  v4f p[C::TM];      // partial sums of subtile column TN - 1, not yet folded
+  float sc[C::TM];   // the chunk's activation scale (x block scale for FPROP / DGRAD)
+  v4f sbj;           // WGRAD: the chunk's row scales of that column
+};
+
+template <int KIND, class C>
+__device__ __forceinline__ void fold(v4f& acc, const v4f& pc, float sc, const v4f& sbj) {
+  if constexpr (KIND == KIND_WGRAD) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pc[r] * sbj[r], sc, acc[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pc[r], sc, acc[r]);
+  }
+}
+
+// One K-chunk of the wave's WM x WN tile from one LDS stage: per 16x16
+// subtile one MFMA (the chunk's partial sum) and four FMAs folding it into the
+// FP32 accumulator with the chunk's scales. `after_reads` runs once the
+// fragment reads are issued (it issues the next chunk's DMA). Folds lag one
+// MFMA behind, so the matrix core always has work queued while the VALU folds.
+template <int KIND, class C, bool HAVE_CARRY, class AfterReads>
+__device__ __forceinline__ void compute_chunk(const uint8_t* __restrict__ As, v4f (&acc)[C::TM][C::TN],
+                                              Carry<KIND, C>& carry, int wave_m, int wave_n, int l16,
+                                              int lq, int off0, int off1, AfterReads after_reads) {
   const uint8_t* Bs = As + kABytes;
   const float* Sa = reinterpret_cast<const float*>(As + kSaOff);
   const float* Sb = reinterpret_cast<const float*>(As + kSbOff);
 
-  float sc[TM];
+  v8i af[C::TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sc[i] = Sa[wave_m * WM + i * 16 + l16];
+  for (int i = 0; i < C::TM; ++i) af[i] = frag(As + (wave_m * C::WM + i * 16) * BK, off0, off1);
+  v8i bcur = frag(Bs + (wave_n * C::WN) * BK, off0, off1);
+  float sc[C::TM];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
   if constexpr (KIND != KIND_WGRAD) {
     const float sbv = Sb[wave_n];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sc[i] *= sbv;
+    for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
   }
+  after_reads();
 
-  v8i af[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const uint8_t* rowp = As + (wave_m * WM + i * 16) * BK;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + off0);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(rowp + off1);
-    af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-  }
-  auto load_b = [&](int j) {
-    const uint8_t* rowp = Bs + (wave_n * WN + j * 16) * BK;
-    const uint4 y0 = *reinterpret_cast<const uint4*>(rowp + off0);
-    const uint4 y1 = *reinterpret_cast<const uint4*>(rowp + off1);
-    return v8i{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-  };
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f sbj[2];
+  v4f prev = zero;
+  // MFMAs in linear order t = j * TM + i; after MFMA t the result of t - 1 is
+  // folded, unless t - 1 lies in the last column (carried to the next chunk).
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const v8i bf = load_b(j);
-    v4f sbj;
-    if constexpr (KIND == KIND_WGRAD) sbj = *reinterpret_cast<const v4f*>(Sb + wave_n * WN + j * 16 + 4 * lq);
+  for (int j = 0; j < C::TN; ++j) {
+    v8i bnext = bcur;
+    if (j + 1 < C::TN) bnext = frag(Bs + (wave_n * C::WN + (j + 1) * 16) * BK, off0, off1);
+    if constexpr (KIND == KIND_WGRAD)
+      sbj[j & 1] = *reinterpret_cast<const v4f*>(Sb + wave_n * C::WN + j * 16 + 4 * lq);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
-      if constexpr (KIND == KIND_WGRAD) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pc[r] * sbj[r], sc[i], acc[i][j][r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pc[r], sc[i], acc[i][j][r]);
+    for (int i = 0; i < C::TM; ++i) {
+      const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], zero, 0, 0, 0, 0, 0, 0);
+      if constexpr (HAVE_CARRY) {
+        if (j == 0) fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
       }
+      const int t = j * C::TM + i;
+      if (t >= 1) {
+        const int pj = (t - 1) / C::TM, pi = (t - 1) % C::TM;
+        if (pj < C::TN - 1) fold<KIND, C>(acc[pi][pj], prev, sc[pi], sbj[pj & 1]);
+      }
+      if (j == C::TN - 1) carry.p[i] = pc;
+      prev = pc;
     }
+    bcur = bnext;
   }
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) carry.sc[i] = sc[i];
+  if constexpr (KIND == KIND_WGRAD) carry.sbj = sbj[(C::TN - 1) & 1];
 }
 
-template <int KIND, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, GroupArgs g) {
+template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
+  using C = Cfg<WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave % kWavesM;
-  const int wave_n = wave / kWavesM;
+  const int wave_m = wave % WAVES_M;
+  const int wave_n = wave / WAVES_M;
   const int l16 = lane & 15, lq = lane >> 4;
 
   int tmi, tni;
@@ -203,88 +248,97 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, GroupArgs g)
   const int nc = (int)(p.k / BK);
 
   // ---- per-thread load descriptors (global -> LDS) -------------------------
-  // Instruction i of wave w covers tile rows [64 i + 8 w, +8); lane ln fills row
-  // 64 i + 8 w + ln / 8, physical slot ln % 8, i.e. logical slot (ln % 8) ^ (row & 7).
-  // Offsets are 32-bit relative to the tile's first row (the host checks that
-  // 256 rows of either operand span less than 2 GiB).
+  // Round i of wave w covers tile rows [i * kRowsPerRound + 8 w, +8); lane ln
+  // fills row ... + ln / 8, physical slot ln % 8, i.e. logical slot
+  // (ln % 8) ^ swz(row). Offsets are 32-bit relative to the tile's first
+  // row (the host checks that 256 rows of either operand span less than 2 GiB);
+  // rows past the end of the operand repeat its last row (their results are
+  // never stored).
   const uint8_t* a_tile = p.a + m0 * p.lda;
   const uint8_t* b_tile = bmat + n0 * p.ldb;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[C::kRounds], b_off[C::kRounds];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 64 * i + 8 * wave + (lane >> 3);
-    const int gslot = (lane & 7) ^ (row & 7);
+  for (int i = 0; i < C::kRounds; ++i) {
+    const int row = i * C::kRowsPerRound + 8 * wave + (lane >> 3);
+    const int gslot = (lane & 7) ^ swz(row);
     const int64_t ar = min(m0 + row, m_end - 1) - m0;
     const int64_t br = min(n0 + row, n_end - 1) - n0;
     a_off[i] = (uint32_t)(ar * p.lda + gslot * 16);
     b_off[i] = (uint32_t)(br * p.ldb + gslot * 16);
   }
-  // Scales: waves 0-3 fetch 64 activation scales each; wave 4 (block scales) or
-  // waves 4-7 (row scales) the weight side. s_base advances s_step floats per chunk.
-  const float* s_base;
-  uint32_t s_off;
-  int64_t s_step;
-  if (wave < 4) {
-    s_base = p.sa + m0;
-    s_off = (uint32_t)(min(m0 + 64 * wave + lane, m_end - 1) - m0) * 4u;
-    s_step = p.ldsa;
-  } else if (KIND == KIND_WGRAD) {
-    s_base = sbm + n0;
-    s_off = (uint32_t)(min(n0 + 64 * (wave - 4) + lane, n_end - 1) - n0) * 4u;
-    s_step = p.ldsb;
-  } else {
-    // two 128-column weight blocks per tile; lanes beyond 0 read block 1 (clamped)
-    const int64_t blk0 = n0 / 128;
-    const int64_t blk = min(blk0 + (lane < 1 ? 0 : 1), n_end / 128 - 1) - blk0;
-    if (KIND == KIND_FPROP) { s_base = sbm + blk0 * p.ldsb; s_off = (uint32_t)(blk * p.ldsb) * 4u; s_step = 1; }
-    else                    { s_base = sbm + blk0;          s_off = (uint32_t)blk * 4u;            s_step = p.ldsb; }
-  }
-  const bool loads_scales = wave < 4 || KIND == KIND_WGRAD || wave == 4;
-  const uint32_t s_lds = wave < 4 ? kSaOff + 256 * wave : kSbOff + 256 * (wave - 4);
-  const uint32_t smem_lds = lds_addr(smem);
-
+  // Scales: four dword DMAs of 64 lanes bring the tile's 256 activation scales
+  // per chunk (waves take turns); the weight side is four more for row scales
+  // (WGRAD) or one for the two block scales of the tile (FPROP / DGRAD).
+  const int64_t blk0 = n0 / 128;
+  const int64_t blk1 = min(blk0 + 1, n_end / 128 - 1) - blk0;   // 0 when the tile has one block
   auto issue = [&](int c) {
-    const uint32_t base = smem_lds + (uint32_t)((c & 1) * kStage);
+    const uint32_t base = lds_addr(smem) + (uint32_t)((c & 1) * kStage);
     const uint8_t* ak = a_tile + (int64_t)c * BK;
     const uint8_t* bk = b_tile + (int64_t)c * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(ak, a_off[i], base + (64 * i + 8 * wave) * BK);
+    for (int i = 0; i < C::kRounds; ++i) dma16(ak, a_off[i], base + (i * C::kRowsPerRound + 8 * wave) * BK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(bk, b_off[i], base + kABytes + (64 * i + 8 * wave) * BK);
-    if (loads_scales) dma4(s_base + c * s_step, s_off, base + s_lds);
+    for (int i = 0; i < C::kRounds; ++i) dma16(bk, b_off[i], base + kABytes + (i * C::kRowsPerRound + 8 * wave) * BK);
+#pragma unroll
+    for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
+      const uint32_t ro = (uint32_t)(min(m0 + 64 * q4 + lane, m_end - 1) - m0) * 4u;
+      dma4(p.sa + m0 + (int64_t)c * p.ldsa, ro, base + kSaOff + 256 * q4);
+    }
+    if constexpr (KIND == KIND_WGRAD) {
+#pragma unroll
+      for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
+        const uint32_t co = (uint32_t)(min(n0 + 64 * q4 + lane, n_end - 1) - n0) * 4u;
+        dma4(sbm + n0 + (int64_t)c * p.ldsb, co, base + kSbOff + 256 * q4);
+      }
+    } else if (wave == C::kWaves - 1) {
+      // lane 0 -> block blk0, every other lane -> block blk0 + blk1
+      const int64_t b = lane < 1 ? 0 : blk1;
+      if constexpr (KIND == KIND_FPROP)
+        dma4(sbm + blk0 * p.ldsb + c, (uint32_t)(b * p.ldsb) * 4u, base + kSbOff);
+      else
+        dma4(sbm + blk0 + (int64_t)c * p.ldsb, (uint32_t)b * 4u, base + kSbOff);
+    }
   };
 
-  v4f acc[TM][TN];
+  v4f acc[C::TM][C::TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
   // first row is a multiple of 16: row r = base + l16, logical slots 2 lq, 2 lq + 1.
-  const int sw = l16 & 7;
+  const int sw = swz(l16);   // the subtile's first row is a multiple of 16
   const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
   const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
 
   // Chunk c lives in stage c % 2. After the barrier at the top of step c every
-  // wave has finished step c - 1, so stage (c + 1) % 2 can be refilled.
+  // wave has finished reading stage (c + 1) % 2 (step c - 1), so the DMA for
+  // chunk c + 1 may refill it; it is issued once this step's fragment reads are.
+  Carry<KIND, C> carry;
   issue(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  compute_chunk<KIND, C, false>(smem, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
+                                [&] { if (nc > 1) issue(1); });
 #pragma clang loop unroll(disable)
-  for (int c = 0; c < nc; ++c) {
+  for (int c = 1; c < nc; ++c) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (c + 1 < nc) issue(c + 1);
-    compute_chunk<KIND>(smem + (c & 1) * kStage, acc, wave_m, wave_n, l16, lq, off0, off1);
+    compute_chunk<KIND, C, true>(smem + (c & 1) * kStage, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
+                                 [&] { if (c + 1 < nc) issue(c + 1); });
   }
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
 
   // ---- epilogue: lane holds out[row][col .. col+3] for each (i, j) ---------
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t row = m0 + wave_m * WM + i * 16 + l16;
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t row = m0 + wave_m * C::WM + i * 16 + l16;
     if (row >= m_end) continue;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t col = n0 + wave_n * WN + j * 16 + 4 * lq;
+    for (int j = 0; j < C::TN; ++j) {
+      const int64_t col = n0 + wave_n * C::WN + j * 16 + 4 * lq;
       if (col >= n_end) continue;
       if constexpr (KIND == KIND_WGRAD) {
         float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
@@ -316,6 +370,10 @@ GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t ld
   return p;
 }
 
+constexpr int kWM = 4;   // 4 x 2 waves of 64 x 128: the accumulator must stay within the
+constexpr int kWN = 2;   // 256 VGPRs the VALU can address, with room for fragments
+constexpr int kBlock = Cfg<kWM, kWN>::kThreads;
+
 }  // namespace
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
@@ -324,11 +382,11 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
   GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   GroupArgs g;
   g.groups = 0;
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kThreads);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kBlock);
   switch (kind) {
-    case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false>), grid, block, 0, st, p, g); break;
-    case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false>), grid, block, 0, st, p, g); break;
-    default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false>), grid, block, 0, st, p, g); break;
+    case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN>), grid, block, 0, st, p, g); break;
+    case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN>), grid, block, 0, st, p, g); break;
+    default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false, kWM, kWN>), grid, block, 0, st, p, g); break;
   }
   return hipGetLastError();
 }
@@ -350,8 +408,8 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, in
   GemmArgs p = make_args(row_off[groups], n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   p.tiles_m = tiles;
   if (tiles == 0) return hipSuccess;   // every group empty: nothing to compute
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kThreads);
-  hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true>), grid, block, 0, st, p, g);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kBlock);
+  hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN>), grid, block, 0, st, p, g);
   return hipGetLastError();
 }
 
