@@ -32,9 +32,10 @@
 //    consecutive rows at one logical slot; measured on gfx950, ds_read_b128
 //    runs at full LDS bandwidth only if rows r and r + 8 also land in different
 //    slots (an (r & 7) swizzle alone halves it).
-//  * Workgroups are remapped so that each XCD (own L2) gets a contiguous range
-//    of output tiles, walked in groups of 8 row-tiles: the blocks resident on
-//    one XCD share activation and weight panels in its L2.
+//  * Persistent workgroups, one per CU; each XCD (own L2) walks a contiguous
+//    range of output tiles in groups of 8 row-tiles, so the blocks resident on
+//    one XCD share activation and weight panels in its L2. The next tile's
+//    first chunk is fetched during the current tile's last chunk.
 #include "internal.h"
 
 namespace fp8bq {
@@ -103,22 +104,6 @@ __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 
-// Tile position: logical tile index after the XCD remap and the grouped walk.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  const int w = blockIdx.x;
-  const int q = T / kXcds, r = T % kXcds;
-  const int xcd = w % kXcds, local = w / kXcds;
-  const int logical = xcd * q + (xcd < r ? xcd : r) + local;
-  const int per_group = kGroupM * tiles_n;
-  const int group = logical / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = logical - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-
 // Physical-slot XOR of LDS row r (see the layout note at the top).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -132,11 +117,14 @@ __device__ __forceinline__ v8i frag(const uint8_t* rowp, int off0, int off1) {
 // subtile's MFMA results of a chunk are folded at the start of the next chunk,
 // after the barrier, so those MFMAs keep the matrix core busy while the waves
 // synchronise.
+// WGRAD folds every column inside its chunk: it needs two VALU ops per output
+// and per-column row scales, and the carry would not fit in its registers.
 template <int KIND, class C>
 struct Carry {
+  static constexpr bool kUsed = KIND != KIND_WGRAD;
   v4f p[C::TM];      // partial sums of subtile column TN - 1, not yet folded
-  float sc[C::TM];   // the chunk's activation scale (x block scale for FPROP / DGRAD)
-  v4f sbj;           // WGRAD: the chunk's row scales of that column
+  float sc[C::TM];   // the chunk's activation scale times the weight block scale
+  v4f sbj;           // unused (kept so that fold() has one signature)
 };
 
 template <int KIND, class C>
@@ -191,24 +179,72 @@ __device__ __forceinline__ void compute_chunk(const uint8_t* __restrict__ As, v4
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], zero, 0, 0, 0, 0, 0, 0);
-      if constexpr (HAVE_CARRY) {
+      if constexpr (HAVE_CARRY && Carry<KIND, C>::kUsed) {
         if (j == 0) fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
       }
       const int t = j * C::TM + i;
       if (t >= 1) {
         const int pj = (t - 1) / C::TM, pi = (t - 1) % C::TM;
-        if (pj < C::TN - 1) fold<KIND, C>(acc[pi][pj], prev, sc[pi], sbj[pj & 1]);
+        if (!Carry<KIND, C>::kUsed || pj < C::TN - 1) fold<KIND, C>(acc[pi][pj], prev, sc[pi], sbj[pj & 1]);
       }
-      if (j == C::TN - 1) carry.p[i] = pc;
+      if (Carry<KIND, C>::kUsed && j == C::TN - 1) carry.p[i] = pc;
       prev = pc;
     }
     bcur = bnext;
   }
+  if constexpr (Carry<KIND, C>::kUsed) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) carry.sc[i] = sc[i];
-  if constexpr (KIND == KIND_WGRAD) carry.sbj = sbj[(C::TN - 1) & 1];
+    for (int i = 0; i < C::TM; ++i) carry.sc[i] = sc[i];
+  } else {
+    fold<KIND, C>(acc[C::TM - 1][C::TN - 1], prev, sc[C::TM - 1], sbj[(C::TN - 1) & 1]);
+  }
 }
 
+// One output tile: its row / column ranges and the weight (with scales) it uses.
+struct Tile {
+  int64_t m0, m_end, n0, n_end;
+  const uint8_t* b;
+  const float* sb;
+};
+
+template <bool GROUPED>
+__device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g, int logical) {
+  const int per_group = kGroupM * p.tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * per_group;
+  const int tmi = first_m + in_group % gsize;
+  const int tni = in_group / gsize;
+  Tile t;
+  t.b = p.b;
+  t.sb = p.sb;
+  if constexpr (GROUPED) {
+    int lo = 0, hi = g.groups;             // find e: tile_prefix[e] <= tmi < tile_prefix[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.tile_prefix[mid] <= tmi) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    t.m0 = (int64_t)g.row_off128[e] * 128 + (int64_t)(tmi - g.tile_prefix[e]) * BM;
+    t.m_end = min(t.m0 + BM, (int64_t)g.row_off128[e + 1] * 128);
+    t.b += (int64_t)e * p.n * p.ldb;
+    t.sb += (int64_t)e * (p.n / 128) * p.ldsb;
+  } else {
+    t.m0 = (int64_t)tmi * BM;
+    t.m_end = min(t.m0 + BM, p.m);
+  }
+  t.n0 = (int64_t)tni * BN;
+  t.n_end = min(t.n0 + BN, p.n);
+  return t;
+}
+
+// Persistent kernel: each workgroup owns one CU and walks a strided list of
+// output tiles. Workgroup w runs on XCD w % 8 (hardware round-robin); the
+// tiles of XCD x are a contiguous range of the grouped walk, shared out among
+// that XCD's workgroups, so blocks resident on one XCD (one L2) work on
+// neighbouring tiles. The first chunk of the next tile is fetched during the
+// current tile's last chunk, so the pipeline fills once per workgroup.
 template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
   using C = Cfg<WAVES_M, WAVES_N>;
@@ -221,31 +257,17 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const int wave_n = wave / WAVES_M;
   const int l16 = lane & 15, lq = lane >> 4;
 
-  int tmi, tni;
-  tile_coords(p.tiles_m, p.tiles_n, tmi, tni);
-
-  // Row range of this tile, and the weight (and its scales) it multiplies.
-  int64_t m0, m_end;
-  const uint8_t* bmat = p.b;
-  const float* sbm = p.sb;
-  if constexpr (GROUPED) {
-    int lo = 0, hi = g.groups;             // find e: tile_prefix[e] <= tmi < tile_prefix[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (g.tile_prefix[mid] <= tmi) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    m0 = (int64_t)g.row_off128[e] * 128 + (int64_t)(tmi - g.tile_prefix[e]) * BM;
-    m_end = min(m0 + BM, (int64_t)g.row_off128[e + 1] * 128);
-    bmat += (int64_t)e * p.n * p.ldb;
-    sbm += (int64_t)e * (p.n / 128) * p.ldsb;
-  } else {
-    m0 = (int64_t)tmi * BM;
-    m_end = min(m0 + BM, p.m);
-  }
-  const int64_t n0 = (int64_t)tni * BN;
-  const int64_t n_end = min(n0 + BN, p.n);
+  // this workgroup's tiles: logical start + local + nper * k, k = 0, 1, ...
+  const int G = gridDim.x, w = blockIdx.x;
+  const int T = p.tiles_m * p.tiles_n;
+  const int x = w % kXcds, local = w / kXcds;
+  const int nper = G / kXcds + (x < G % kXcds ? 1 : 0);
+  const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
+  const int start = x * (T / kXcds) + min(x, T % kXcds);
+  if (local >= count) return;                                  // uniform: no tile for this workgroup
+  const int my_tiles = (count - local + nper - 1) / nper;
   const int nc = (int)(p.k / BK);
+  const int total = my_tiles * nc;
 
   // ---- per-thread load descriptors (global -> LDS) -------------------------
   // Round i of wave w covers tile rows [i * kRowsPerRound + 8 w, +8); lane ln
@@ -254,49 +276,51 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   // row (the host checks that 256 rows of either operand span less than 2 GiB);
   // rows past the end of the operand repeat its last row (their results are
   // never stored).
-  const uint8_t* a_tile = p.a + m0 * p.lda;
-  const uint8_t* b_tile = bmat + n0 * p.ldb;
   uint32_t a_off[C::kRounds], b_off[C::kRounds];
+  auto set_offsets = [&](const Tile& t) {
 #pragma unroll
-  for (int i = 0; i < C::kRounds; ++i) {
-    const int row = i * C::kRowsPerRound + 8 * wave + (lane >> 3);
-    const int gslot = (lane & 7) ^ swz(row);
-    const int64_t ar = min(m0 + row, m_end - 1) - m0;
-    const int64_t br = min(n0 + row, n_end - 1) - n0;
-    a_off[i] = (uint32_t)(ar * p.lda + gslot * 16);
-    b_off[i] = (uint32_t)(br * p.ldb + gslot * 16);
-  }
-  // Scales: four dword DMAs of 64 lanes bring the tile's 256 activation scales
-  // per chunk (waves take turns); the weight side is four more for row scales
-  // (WGRAD) or one for the two block scales of the tile (FPROP / DGRAD).
-  const int64_t blk0 = n0 / 128;
-  const int64_t blk1 = min(blk0 + 1, n_end / 128 - 1) - blk0;   // 0 when the tile has one block
-  auto issue = [&](int c) {
-    const uint32_t base = lds_addr(smem) + (uint32_t)((c & 1) * kStage);
-    const uint8_t* ak = a_tile + (int64_t)c * BK;
-    const uint8_t* bk = b_tile + (int64_t)c * BK;
+    for (int i = 0; i < C::kRounds; ++i) {
+      const int row = i * C::kRowsPerRound + 8 * wave + (lane >> 3);
+      const int gslot = (lane & 7) ^ swz(row);
+      const int64_t ar = min(t.m0 + row, t.m_end - 1) - t.m0;
+      const int64_t br = min(t.n0 + row, t.n_end - 1) - t.n0;
+      a_off[i] = (uint32_t)(ar * p.lda + gslot * 16);
+      b_off[i] = (uint32_t)(br * p.ldb + gslot * 16);
+    }
+  };
+  // Chunk c of tile t into LDS stage st. Scales: four dword DMAs of 64 lanes
+  // bring the tile's 256 activation scales (waves take turns); the weight side
+  // is four more for row scales (WGRAD) or one for the two block scales of the
+  // tile (FPROP / DGRAD).
+  auto issue = [&](const Tile& t, int c, int st) {
+    const uint32_t base = lds_addr(smem) + (uint32_t)(st * kStage);
+    const uint8_t* ak = p.a + t.m0 * p.lda + (int64_t)c * BK;
+    const uint8_t* bk = t.b + t.n0 * p.ldb + (int64_t)c * BK;
 #pragma unroll
     for (int i = 0; i < C::kRounds; ++i) dma16(ak, a_off[i], base + (i * C::kRowsPerRound + 8 * wave) * BK);
 #pragma unroll
     for (int i = 0; i < C::kRounds; ++i) dma16(bk, b_off[i], base + kABytes + (i * C::kRowsPerRound + 8 * wave) * BK);
 #pragma unroll
     for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
-      const uint32_t ro = (uint32_t)(min(m0 + 64 * q4 + lane, m_end - 1) - m0) * 4u;
-      dma4(p.sa + m0 + (int64_t)c * p.ldsa, ro, base + kSaOff + 256 * q4);
+      const uint32_t ro = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
+      dma4(p.sa + t.m0 + (int64_t)c * p.ldsa, ro, base + kSaOff + 256 * q4);
     }
     if constexpr (KIND == KIND_WGRAD) {
 #pragma unroll
       for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
-        const uint32_t co = (uint32_t)(min(n0 + 64 * q4 + lane, n_end - 1) - n0) * 4u;
-        dma4(sbm + n0 + (int64_t)c * p.ldsb, co, base + kSbOff + 256 * q4);
+        const uint32_t co = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
+        dma4(t.sb + t.n0 + (int64_t)c * p.ldsb, co, base + kSbOff + 256 * q4);
       }
     } else if (wave == C::kWaves - 1) {
-      // lane 0 -> block blk0, every other lane -> block blk0 + blk1
+      // lane 0 -> the tile's first 128-column block, every other lane -> its
+      // second (the first again when the tile has only one)
+      const int64_t blk0 = t.n0 / 128;
+      const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
       const int64_t b = lane < 1 ? 0 : blk1;
       if constexpr (KIND == KIND_FPROP)
-        dma4(sbm + blk0 * p.ldsb + c, (uint32_t)(b * p.ldsb) * 4u, base + kSbOff);
+        dma4(t.sb + blk0 * p.ldsb + c, (uint32_t)(b * p.ldsb) * 4u, base + kSbOff);
       else
-        dma4(sbm + blk0 + (int64_t)c * p.ldsb, (uint32_t)b * 4u, base + kSbOff);
+        dma4(t.sb + blk0 + (int64_t)c * p.ldsb, (uint32_t)b * 4u, base + kSbOff);
     }
   };
 
@@ -312,48 +336,79 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
   const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
 
-  // Chunk c lives in stage c % 2. After the barrier at the top of step c every
-  // wave has finished reading stage (c + 1) % 2 (step c - 1), so the DMA for
-  // chunk c + 1 may refill it; it is issued once this step's fragment reads are.
+  // Step s handles chunk c = s % nc of the workgroup's (s / nc)-th tile from
+  // stage s % 2. After the barrier at the top of step s every wave has finished
+  // step s - 1, so stage (s + 1) % 2 may be refilled: with the next chunk of the
+  // same tile, or with chunk 0 of the next tile during a tile's last chunk.
+  // The carried column is zero at a tile's first chunk, so folding it there is
+  // a no-op and every step runs the same code.
   Carry<KIND, C> carry;
-  issue(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  compute_chunk<KIND, C, false>(smem, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
-                                [&] { if (nc > 1) issue(1); });
-#pragma clang loop unroll(disable)
-  for (int c = 1; c < nc; ++c) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute_chunk<KIND, C, true>(smem + (c & 1) * kStage, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
-                                 [&] { if (c + 1 < nc) issue(c + 1); });
-  }
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
-
-  // ---- epilogue: lane holds out[row][col .. col+3] for each (i, j) ---------
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
-    const int64_t row = m0 + wave_m * C::WM + i * 16 + l16;
-    if (row >= m_end) continue;
+    carry.p[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    carry.sc[i] = 0.f;
+  }
+  carry.sbj = v4f{0.f, 0.f, 0.f, 0.f};
+  int tk = 0;
+  Tile cur = make_tile<GROUPED>(p, g, start + local);
+  Tile nxt = cur;
+  set_offsets(cur);
+  issue(cur, 0, 0);
+  int c = 0;
+#pragma clang loop unroll(disable)
+  for (int s = 0; s < total; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const bool last = c + 1 == nc;
+    const bool more = !last || tk + 1 < my_tiles;
+    if (last && more) {
+      nxt = make_tile<GROUPED>(p, g, start + local + nper * (tk + 1));
+      set_offsets(nxt);                        // the current tile issues no more loads
+    }
+    const Tile& tt = last ? nxt : cur;
+    const int cc = last ? 0 : c + 1;
+    compute_chunk<KIND, C, true>(smem + (s & 1) * kStage, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
+                                 [&] { if (more) issue(tt, cc, (s + 1) & 1); });
+    if (!last) {
+      ++c;
+      continue;
+    }
+
+    // ---- tile done: last column's fold, epilogue, next tile ----------------
+    if constexpr (Carry<KIND, C>::kUsed) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int64_t col = n0 + wave_n * C::WN + j * 16 + 4 * lq;
-      if (col >= n_end) continue;
-      if constexpr (KIND == KIND_WGRAD) {
-        float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
-        *reinterpret_cast<v4f*>(o) = acc[i][j];
-      } else {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t u = __float_as_uint(acc[i][j][r]);
-          h[r] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // round to nearest even (finite)
-        }
-        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
-        *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      for (int i = 0; i < C::TM; ++i) {
+        fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
+        carry.p[i] = v4f{0.f, 0.f, 0.f, 0.f};
       }
     }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const int64_t row = cur.m0 + wave_m * C::WM + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int64_t col = cur.n0 + wave_n * C::WN + j * 16 + 4 * lq;
+        if (row < cur.m_end && col < cur.n_end) {
+          if constexpr (KIND == KIND_WGRAD) {
+            float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
+            *reinterpret_cast<v4f*>(o) = acc[i][j];
+          } else {
+            uint32_t h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t u = __float_as_uint(acc[i][j][r]);
+              h[r] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // round to nearest even (finite)
+            }
+            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          }
+        }
+        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    c = 0;
+    ++tk;
+    cur = nxt;
   }
 }
 
@@ -374,6 +429,18 @@ constexpr int kWM = 4;   // 4 x 2 waves of 64 x 128: the accumulator must stay w
 constexpr int kWN = 2;   // 256 VGPRs the VALU can address, with room for fragments
 constexpr int kBlock = Cfg<kWM, kWN>::kThreads;
 
+// One workgroup per CU (the LDS stages take most of a CU's 160 KB): as many
+// workgroups as CUs, or as tiles when there are fewer tiles.
+int persistent_grid(int tiles) {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return tiles < cus ? tiles : cus;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
@@ -382,7 +449,7 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
   GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   GroupArgs g;
   g.groups = 0;
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kBlock);
+  const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
   switch (kind) {
     case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN>), grid, block, 0, st, p, g); break;
     case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN>), grid, block, 0, st, p, g); break;
@@ -408,7 +475,7 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, in
   GemmArgs p = make_args(row_off[groups], n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   p.tiles_m = tiles;
   if (tiles == 0) return hipSuccess;   // every group empty: nothing to compute
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kBlock);
+  const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
   hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN>), grid, block, 0, st, p, g);
   return hipGetLastError();
 }
