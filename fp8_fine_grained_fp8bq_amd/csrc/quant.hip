@@ -14,15 +14,13 @@
 //    order like the values for finite inputs), reduced across a tile's lanes
 //    with DPP row permutations;
 //  * the exact quotient fl32(x / s) is needed only to pick an E4M3 code. With
-//    r = fl32(1 / s), rlo = fl32(r (1 - 2^-20)), rhi = fl32(r (1 + 2^-20)), the
-//    products x*rlo and x*rhi bracket fl32(x / s) strictly (each of r, rlo/rhi
-//    and the product is within 2^-24 relative, so x*rlo <= (x/s)(1 - 0.81*2^-20)
-//    < fl32(x/s) and symmetrically for rhi, for x / s in fp32's normal range;
-//    below it all three encode to a signed zero). The conversion is monotone,
-//    so when both brackets give the same code it is the code of fl32(x / s).
-//    Otherwise (about 3 elements in 10^5) the lane recomputes with the
-//    correctly-rounded division. Tiles whose scale is below 2^-100 (where
-//    1 / s may overflow) always take the division.
+//    r ~ 1 / s, rlo = fl32(r (1 - 2^-19)), rhi = fl32(r (1 + 2^-19)), the
+//    products x*rlo and x*rhi bracket fl32(x / s) strictly (see make_scale for
+//    the error budget; for x / s below fp32's normal range all three encode to
+//    a signed zero). The conversion is monotone, so when both brackets give
+//    the same code it is the code of fl32(x / s). Otherwise (about 6 elements
+//    in 10^5) the lane recomputes with the correctly-rounded division. Tiles
+//    whose scale is below 2^-100 always take the division.
 //  * v_cvt_pk_fp8_f32 rounds to nearest even, keeps the sign of zero and handles
 //    fp32 denormals like the E4M3 definition on every finite input below 448,
 //    and returns 448 for inputs in [448, 464]. No quotient here exceeds 450
@@ -60,6 +58,18 @@ __device__ __forceinline__ uint32_t mag_max2(uint32_t w) {
   return umax(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Packed (two 16-bit lanes per dword) max of the bf16 magnitudes of 8 dwords;
+// returns the largest of the 16 magnitudes.
+__device__ __forceinline__ uint32_t mag_max16(const uint4 a, const uint4 b) {
+  auto m = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
+  const u16x2 r = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_elementwise_max(m(a.x), m(a.y)), __builtin_elementwise_max(m(a.z), m(a.w))),
+      __builtin_elementwise_max(__builtin_elementwise_max(m(b.x), m(b.y)), __builtin_elementwise_max(m(b.z), m(b.w))));
+  return umax(r.x, r.y);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -75,18 +85,27 @@ struct TileScale {
 };
 
 // Scale of a group from the magnitude bits (upper 16 bits of an fp32) of its absmax.
+//  * s = fl32(amax / 448) without a division: q = fl32(amax * fl32(1/448)) is
+//    corrected once with the exact residual amax - 448 q (an FMA), which gives
+//    the correctly rounded quotient for every bf16 amax (checked for all 32639
+//    positive finite bf16 values, on the CPU and by the GPU parity tests).
+//  * r approximates 1 / s with the hardware reciprocal (documented within 1
+//    ulp); the brackets x * r (1 -+ 2^-19) enclose fl32(x / s) strictly as
+//    long as r is within 13 ulp: e_r + 2 * 2^-24 < 2^-19 - 2^-24.
 __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits16) {
   TileScale t;
   const float amax = __uint_as_float(amax_bits16 << 16);
-  t.s = amax / kFmax;                      // correctly rounded binary32 division
+  const float c = 1.0f / kFmax;                                    // constant-folded
+  const float q = amax * c;
+  t.s = __builtin_fmaf(__builtin_fmaf(-q, kFmax, amax), c, q);     // fl32(amax / 448)
   if (t.s == 0.0f) {
     t.rlo = t.rhi = 0.0f;                  // +-0 * 0 keeps the sign of zero
     t.fast = true;
   } else {
     t.fast = t.s >= kFastScaleMin;
-    const float r = t.fast ? 1.0f / t.s : 0.0f;
-    t.rlo = r * (1.0f - 0x1p-20f);
-    t.rhi = r * (1.0f + 0x1p-20f);
+    const float r = t.fast ? __builtin_amdgcn_rcpf(t.s) : 0.0f;
+    t.rlo = r * (1.0f - 0x1p-19f);
+    t.rhi = r * (1.0f + 0x1p-19f);
   }
   return t;
 }
@@ -110,58 +129,31 @@ __device__ __forceinline__ uint2 encode8(const uint4 w, const TileScale& t) {
 
 // ---------------------------------------------------------------------------
 // 1x128 row-wise activation tiles.
-// One 16-lane DPP row holds one tile (each lane 8 bf16 = 16 B); a wave handles
-// kRowU x 4 consecutive tiles of the flattened [rows, cols/128] grid, so every
-// load instruction of a wave reads 1 KB of consecutive tiles.
+// One tile per aligned group of 8 lanes (each lane 16 bf16 = 32 B, stored as
+// 16 codes = 16 B). Grid: y = 128-column chunk, x = groups of 32 rows; the 8
+// tiles of a wave are 8 consecutive rows of one chunk, so every load
+// instruction reads 8 runs of 256 B and the wave's 8 scales land in 32
+// contiguous bytes of the chunk-major scale array.
 // ---------------------------------------------------------------------------
-constexpr int kRowU = 2;
 constexpr int kRowThreads = 256;
+constexpr int kRowsPerBlock = (kRowThreads / 64) * 8;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// 16-byte load / 8-byte store, optionally marked non-temporal (streamed once).
-__device__ __forceinline__ uint4 load16(const void* p, bool nt) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  const u32x4 v = nt ? __builtin_nontemporal_load(q) : *q;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void store8(void* p, uint2 v, bool nt) {
-  u32x2* q = reinterpret_cast<u32x2*>(p);
-  const u32x2 w = {v.x, v.y};
-  if (nt) __builtin_nontemporal_store(w, q); else *q = w;
-}
-
-template <int U, bool NT>
 __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int tiles_per_row, int ntiles,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds) {
+    const uint16_t* __restrict__ x, int64_t ldx, int rows, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s, int64_t lds) {
   const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4, l16 = lane & 15;
-  const int wave = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
-  const int t0 = wave * (4 * U);
-
-  uint4 v[U];
-  int row[U], col[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    int t = t0 + u * 4 + grp;
-    t = t < ntiles ? t : ntiles - 1;
-    row[u] = t / tiles_per_row;
-    col[u] = t - row[u] * tiles_per_row;
-    v[u] = load16(x + (int64_t)row[u] * ldx + col[u] * 128 + l16 * 8, NT);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    uint32_t m = umax(umax(mag_max2(v[u].x), mag_max2(v[u].y)), umax(mag_max2(v[u].z), mag_max2(v[u].w)));
-    m = row16_max(m);
-    const TileScale ts = make_scale(m);
-    const uint2 codes = encode8(v[u], ts);
-    const int t = t0 + u * 4 + grp;
-    if (t < ntiles) {
-      store8(q + (int64_t)row[u] * ldq + col[u] * 128 + l16 * 8, codes, NT);
-      if (l16 == 0) s[(int64_t)col[u] * lds + row[u]] = ts.s;
-    }
+  const int l8 = lane & 7;
+  const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 3);
+  const int row = r < rows ? r : rows - 1;
+  const int col = blockIdx.y;
+  const uint16_t* p = x + (int64_t)row * ldx + col * 128 + l8 * 16;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(p);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
+  const TileScale ts = make_scale(lane8_max(mag_max16(v0, v1)));
+  const uint2 a = encode8(v0, ts), b = encode8(v1, ts);
+  if (r < rows) {
+    *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + col * 128 + l8 * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    if (l8 == 0) s[(int64_t)col * lds + row] = ts.s;
   }
 }
 
@@ -253,10 +245,8 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   for (int i = 0; i < 8; ++i)
     v[i] = *reinterpret_cast<const uint4*>(w + (n0 + r + 16 * i) * ldw + k0 + c8);
 
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    m = umax(m, umax(umax(mag_max2(v[i].x), mag_max2(v[i].y)), umax(mag_max2(v[i].z), mag_max2(v[i].w))));
+  uint32_t m = umax(umax(mag_max16(v[0], v[1]), mag_max16(v[2], v[3])),
+                    umax(mag_max16(v[4], v[5]), mag_max16(v[6], v[7])));
   m = row16_max(m);
   m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
   m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
@@ -304,12 +294,8 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
 
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
-  const int tiles_per_row = (int)(cols / 128);
-  const int ntiles = (int)(rows * tiles_per_row);
-  const int per_block = (kRowThreads / 64) * 4 * kRowU;
-  const int blocks = (ntiles + per_block - 1) / per_block;
-  hipLaunchKernelGGL((quant_act_rows_kernel<kRowU, false>), dim3(blocks), dim3(kRowThreads), 0, st, x,
-                     ldx, tiles_per_row, ntiles, q, ldq, s, lds);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)(cols / 128));
+  hipLaunchKernelGGL(quant_act_rows_kernel, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, q, ldq, s, lds);
   return hipGetLastError();
 }
 

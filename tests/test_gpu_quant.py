@@ -72,6 +72,19 @@ def test_every_bf16_value_at_arbitrary_scale(amax_bits):
     _assert_act_rows(_all_bf16_upto(amax_bits), name=f"all bf16 up to {amax_bits:#x}")
 
 
+def test_scale_for_every_bf16_absmax():
+    # one tile per positive finite bf16 absmax (32639 of them), alternating signs; the
+    # other elements are fixed fractions of it, so every scale the method can produce
+    # is checked bit for bit, together with its codes
+    amax = np.arange(1, 0x7F80, dtype=np.uint16)
+    a = (amax.astype(np.uint32) << 16).view(np.float32)
+    fr = np.linspace(-1, 1, 127, dtype=np.float32)
+    body = f32_to_bf16_bits(a[:, None] * fr[None, :])          # |body| <= amax
+    signs = np.where(np.arange(amax.size) % 2 == 1, 0x8000, 0).astype(np.uint16)
+    x = np.concatenate([(amax | signs)[:, None], body], axis=1).astype(np.uint16)
+    _assert_act_rows(x, name="every bf16 absmax")
+
+
 def test_edge_tiles():
     x = act(7, 16, 1024, outlier_p=0).copy()
     x[0, 0:128] = 0                                    # all +0
