@@ -70,6 +70,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the GEMM source has
+    changed since the counters were taken (or the summary is missing)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "large_fprop_hbm_traffic.md")
+    src = os.path.join(ROOT, "fp8_fine_grained_fp8bq_amd", "csrc", "gemm.hip")
+    try:
+        kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith("gemm_") and ": " in line)
+        if kv.get("gemm_source_sha256", "").strip() != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return int(kv["gemm_fetch_bytes_per_launch"]) + int(kv["gemm_write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -207,7 +224,8 @@ def main():
         "config": {"workload": name, "M": M, "N": N, "K": K, "act_tile": "1x128", "weight_block": "128x128",
                    "fp8": "E4M3FN", "out": "bf16", "step": "quant_act + quant_w + gemm"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": gemm_traffic() if args.workload == "large" else None,
                      "kernel": "gemm_kernel<FPROP>", "avg_us": round(tg, 2), "median_us": round(tg_med, 2)},
         "cpu_baseline": cpu,
         "breakdown": {
