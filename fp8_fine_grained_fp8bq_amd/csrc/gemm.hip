@@ -65,7 +65,7 @@ struct Cfg {
   static constexpr int kRounds = BM / kRowsPerRound;
   static_assert(WN == 128, "one weight block column per wave");
   static_assert(BM == BN && BM % kRowsPerRound == 0, "tile / wave grid");
-  static_assert(kWaves == 4 || kWaves == 8, "scale loaders: four 64-lane dword DMAs per side");
+  static_assert(kWaves == 8, "scale loaders: four 64-lane dword DMAs per side");
 };
 
 struct GemmArgs {
@@ -104,6 +104,16 @@ __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 
+// A pointer every lane holds the same value of, moved to scalar registers
+// (the LDS-DMA helpers take their base address in SGPRs).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Physical-slot XOR of LDS row r (see the layout note at the top).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -113,21 +123,14 @@ __device__ __forceinline__ v8i frag(const uint8_t* rowp, int off0, int off1) {
   return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-// Per-chunk promotion state carried across the barrier: the last weight
-// subtile's MFMA results of a chunk are folded at the start of the next chunk,
-// after the barrier, so those MFMAs keep the matrix core busy while the waves
-// synchronise.
-// WGRAD folds every column inside its chunk: it needs two VALU ops per output
-// and per-column row scales, and the carry would not fit in its registers.
-template <int KIND, class C>
-struct Carry {
-  static constexpr bool kUsed = KIND != KIND_WGRAD;
-  v4f p[C::TM];      // partial sums of subtile column TN - 1, not yet folded
-  float sc[C::TM];   // the chunk's activation scale times the weight block scale
-  v4f sbj;           // unused (kept so that fold() has one signature)
-};
-
-template <int KIND, class C>
+// Folds one chunk's MFMA result into the FP32 accumulator with the chunk's
+// scales: acc += P * (s_a * s_b). FPROP / DGRAD pass the product of the row's
+// activation scale and the weight block scale in sc; WGRAD has a row scale per
+// output row (sc) and a column scale per output column (sbj).
+// The empty asm pins the fold where it is written: without it the compiler
+// sinks the folds of a whole chunk below the mid-chunk barrier, keeping every
+// MFMA result of the chunk live at once.
+template <int KIND>
 __device__ __forceinline__ void fold(v4f& acc, const v4f& pc, float sc, const v4f& sbj) {
   if constexpr (KIND == KIND_WGRAD) {
 #pragma unroll
@@ -136,68 +139,7 @@ __device__ __forceinline__ void fold(v4f& acc, const v4f& pc, float sc, const v4
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pc[r], sc, acc[r]);
   }
-}
-
-// One K-chunk of the wave's WM x WN tile from one LDS stage: per 16x16
-// subtile one MFMA (the chunk's partial sum) and four FMAs folding it into the
-// FP32 accumulator with the chunk's scales. `after_reads` runs once the
-// fragment reads are issued (it issues the next chunk's DMA). Folds lag one
-// MFMA behind, so the matrix core always has work queued while the VALU folds.
-template <int KIND, class C, bool HAVE_CARRY, class AfterReads>
-__device__ __forceinline__ void compute_chunk(const uint8_t* __restrict__ As, v4f (&acc)[C::TM][C::TN],
-                                              Carry<KIND, C>& carry, int wave_m, int wave_n, int l16,
-                                              int lq, int off0, int off1, AfterReads after_reads) {
-  const uint8_t* Bs = As + kABytes;
-  const float* Sa = reinterpret_cast<const float*>(As + kSaOff);
-  const float* Sb = reinterpret_cast<const float*>(As + kSbOff);
-
-  v8i af[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) af[i] = frag(As + (wave_m * C::WM + i * 16) * BK, off0, off1);
-  v8i bcur = frag(Bs + (wave_n * C::WN) * BK, off0, off1);
-  float sc[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
-  if constexpr (KIND != KIND_WGRAD) {
-    const float sbv = Sb[wave_n];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
-  }
-  after_reads();
-
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  v4f sbj[2];
-  v4f prev = zero;
-  // MFMAs in linear order t = j * TM + i; after MFMA t the result of t - 1 is
-  // folded, unless t - 1 lies in the last column (carried to the next chunk).
-#pragma unroll
-  for (int j = 0; j < C::TN; ++j) {
-    v8i bnext = bcur;
-    if (j + 1 < C::TN) bnext = frag(Bs + (wave_n * C::WN + (j + 1) * 16) * BK, off0, off1);
-    if constexpr (KIND == KIND_WGRAD)
-      sbj[j & 1] = *reinterpret_cast<const v4f*>(Sb + wave_n * C::WN + j * 16 + 4 * lq);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], zero, 0, 0, 0, 0, 0, 0);
-      if constexpr (HAVE_CARRY && Carry<KIND, C>::kUsed) {
-        if (j == 0) fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
-      }
-      const int t = j * C::TM + i;
-      if (t >= 1) {
-        const int pj = (t - 1) / C::TM, pi = (t - 1) % C::TM;
-        if (!Carry<KIND, C>::kUsed || pj < C::TN - 1) fold<KIND, C>(acc[pi][pj], prev, sc[pi], sbj[pj & 1]);
-      }
-      if (Carry<KIND, C>::kUsed && j == C::TN - 1) carry.p[i] = pc;
-      prev = pc;
-    }
-    bcur = bnext;
-  }
-  if constexpr (Carry<KIND, C>::kUsed) {
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) carry.sc[i] = sc[i];
-  } else {
-    fold<KIND, C>(acc[C::TM - 1][C::TN - 1], prev, sc[C::TM - 1], sbj[(C::TN - 1) & 1]);
-  }
+  asm volatile("" : "+v"(acc));
 }
 
 // One output tile: its row / column ranges and the weight (with scales) it uses.
@@ -269,14 +211,17 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const int nc = (int)(p.k / BK);
   const int total = my_tiles * nc;
 
-  // ---- per-thread load descriptors (global -> LDS) -------------------------
+  // ---- per-lane load offsets of one tile (global -> LDS) --------------------
   // Round i of wave w covers tile rows [i * kRowsPerRound + 8 w, +8); lane ln
   // fills row ... + ln / 8, physical slot ln % 8, i.e. logical slot
   // (ln % 8) ^ swz(row). Offsets are 32-bit relative to the tile's first
   // row (the host checks that 256 rows of either operand span less than 2 GiB);
   // rows past the end of the operand repeat its last row (their results are
-  // never stored).
-  uint32_t a_off[C::kRounds], b_off[C::kRounds];
+  // never stored). Scales: waves 0-3 bring 64 activation scales each; waves
+  // 4-7 bring 64 column scales each (WGRAD) or the tile's two weight block
+  // scales (lane 0 the first block, the other lanes the second, which is the
+  // first again when the tile has only one; waves 5-7 write unused copies).
+  uint32_t a_off[C::kRounds], b_off[C::kRounds], s_off;
   auto set_offsets = [&](const Tile& t) {
 #pragma unroll
     for (int i = 0; i < C::kRounds; ++i) {
@@ -287,48 +232,69 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
       a_off[i] = (uint32_t)(ar * p.lda + gslot * 16);
       b_off[i] = (uint32_t)(br * p.ldb + gslot * 16);
     }
-  };
-  // Chunk c of tile t into LDS stage st. Scales: four dword DMAs of 64 lanes
-  // bring the tile's 256 activation scales (waves take turns); the weight side
-  // is four more for row scales (WGRAD) or one for the two block scales of the
-  // tile (FPROP / DGRAD).
-  auto issue = [&](const Tile& t, int c, int st) {
-    const uint32_t base = lds_addr(smem) + (uint32_t)(st * kStage);
-    const uint8_t* ak = p.a + t.m0 * p.lda + (int64_t)c * BK;
-    const uint8_t* bk = t.b + t.n0 * p.ldb + (int64_t)c * BK;
-#pragma unroll
-    for (int i = 0; i < C::kRounds; ++i) dma16(ak, a_off[i], base + (i * C::kRowsPerRound + 8 * wave) * BK);
-#pragma unroll
-    for (int i = 0; i < C::kRounds; ++i) dma16(bk, b_off[i], base + kABytes + (i * C::kRowsPerRound + 8 * wave) * BK);
-#pragma unroll
-    for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
-      const uint32_t ro = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
-      dma4(p.sa + t.m0 + (int64_t)c * p.ldsa, ro, base + kSaOff + 256 * q4);
-    }
-    if constexpr (KIND == KIND_WGRAD) {
-#pragma unroll
-      for (int q4 = wave; q4 < 4; q4 += C::kWaves) {
-        const uint32_t co = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
-        dma4(t.sb + t.n0 + (int64_t)c * p.ldsb, co, base + kSbOff + 256 * q4);
-      }
-    } else if (wave == C::kWaves - 1) {
-      // lane 0 -> the tile's first 128-column block, every other lane -> its
-      // second (the first again when the tile has only one)
+    const int q4 = wave & 3;
+    if (wave < 4) {
+      s_off = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
+    } else if constexpr (KIND == KIND_WGRAD) {
+      s_off = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
+    } else {
       const int64_t blk0 = t.n0 / 128;
       const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
-      const int64_t b = lane < 1 ? 0 : blk1;
-      if constexpr (KIND == KIND_FPROP)
-        dma4(t.sb + blk0 * p.ldsb + c, (uint32_t)(b * p.ldsb) * 4u, base + kSbOff);
-      else
-        dma4(t.sb + blk0 + (int64_t)c * p.ldsb, (uint32_t)b * 4u, base + kSbOff);
+      const int64_t bsel = lane < 1 ? 0 : blk1;
+      s_off = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
     }
   };
 
-  v4f acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // ---- global -> LDS cursor: runs two steps ahead of the MFMAs -------------
+  // Step s is chunk s % nc of the workgroup's (s / nc)-th tile and lives in
+  // stage s % 2. The cursor (dtk, dc) is the next step to load; d_ak, d_bk,
+  // d_sk point at its chunk of A, B and the wave's scale vector. A step goes
+  // out as kParts load instructions per wave, issued one per MFMA by part(q)
+  // so that no wave stalls on a burst of loads. After the last step the
+  // cursor stays put: the remaining loads repeat that step into a stage no
+  // one reads any more (the kernel waits for them before it ends), which
+  // keeps every load unconditional.
+  constexpr int kParts = 2 * C::kRounds + 1;
+  int dtk = 0, dc = 0;
+  const uint8_t* d_ak;
+  const uint8_t* d_bk;
+  const float* d_sk;
+  // per-step advance of the wave's scale pointer: activation scales are
+  // chunk-major; FPROP block scales are contiguous along K, DGRAD's and the
+  // WGRAD column scales chunk-major
+  const int64_t s_step = wave < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
+  auto cursor_tile = [&]() {
+    const Tile t = make_tile<GROUPED>(p, g, start + local + nper * dtk);
+    set_offsets(t);
+    d_ak = p.a + t.m0 * p.lda;
+    d_bk = t.b + t.n0 * p.ldb;
+    if (wave < 4) d_sk = p.sa + t.m0;
+    else if constexpr (KIND == KIND_WGRAD) d_sk = t.sb + t.n0;
+    else if constexpr (KIND == KIND_FPROP) d_sk = t.sb + (t.n0 / 128) * p.ldsb;
+    else d_sk = t.sb + t.n0 / 128;
+  };
+  auto advance = [&]() {
+    if (dc + 1 < nc) {
+      ++dc;
+      d_ak += BK;
+      d_bk += BK;
+      d_sk += s_step;
+    } else if (dtk + 1 < my_tiles) {
+      dc = 0;
+      ++dtk;
+      cursor_tile();
+    }
+  };
+  cursor_tile();
+  auto part = [&](int q, int st) {
+    const uint32_t base = lds_addr(smem) + (uint32_t)(st * kStage);
+    if (q < C::kRounds)
+      dma16(d_ak, a_off[q], base + (q * C::kRowsPerRound + 8 * wave) * BK);
+    else if (q < 2 * C::kRounds)
+      dma16(d_bk, b_off[q - C::kRounds], base + kABytes + ((q - C::kRounds) * C::kRowsPerRound + 8 * wave) * BK);
+    else
+      dma4(uniform_ptr(d_sk), s_off, base + (wave < 4 ? kSaOff : kSbOff) + 256 * (wave & 3));
+  };
 
   // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
   // first row is a multiple of 16: row r = base + l16, logical slots 2 lq, 2 lq + 1.
@@ -336,52 +302,150 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
   const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
 
-  // Step s handles chunk c = s % nc of the workgroup's (s / nc)-th tile from
-  // stage s % 2. After the barrier at the top of step s every wave has finished
-  // step s - 1, so stage (s + 1) % 2 may be refilled: with the next chunk of the
-  // same tile, or with chunk 0 of the next tile during a tile's last chunk.
-  // The carried column is zero at a tile's first chunk, so folding it there is
-  // a no-op and every step runs the same code.
-  Carry<KIND, C> carry;
+  // Fragments and scales of one step, read from its stage: the wave's TM
+  // activation subtiles, the first weight subtile and the per-row scale
+  // products of the chunk.
+  auto read_scales = [&](const uint8_t* stage, float (&sc)[C::TM]) {
+    const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
+    const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    carry.p[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    carry.sc[i] = 0.f;
-  }
-  carry.sbj = v4f{0.f, 0.f, 0.f, 0.f};
-  int tk = 0;
-  Tile cur = make_tile<GROUPED>(p, g, start + local);
-  Tile nxt = cur;
-  set_offsets(cur);
-  issue(cur, 0, 0);
-  int c = 0;
-#pragma clang loop unroll(disable)
-  for (int s = 0; s < total; ++s) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const bool last = c + 1 == nc;
-    const bool more = !last || tk + 1 < my_tiles;
-    if (last && more) {
-      nxt = make_tile<GROUPED>(p, g, start + local + nper * (tk + 1));
-      set_offsets(nxt);                        // the current tile issues no more loads
+    for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
+    if constexpr (KIND != KIND_WGRAD) {
+      const float sbv = Sb[wave_n];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
     }
-    const Tile& tt = last ? nxt : cur;
-    const int cc = last ? 0 : c + 1;
-    compute_chunk<KIND, C, true>(smem + (s & 1) * kStage, acc, carry, wave_m, wave_n, l16, lq, off0, off1,
-                                 [&] { if (more) issue(tt, cc, (s + 1) & 1); });
-    if (!last) {
-      ++c;
-      continue;
+  };
+  auto wgrad_col_scales = [&](const uint8_t* stage, int j) {
+    return *reinterpret_cast<const v4f*>(stage + kSbOff + 4 * (wave_n * C::WN + j * 16 + 4 * lq));
+  };
+  auto a_frag = [&](const uint8_t* stage, int i) { return frag(stage + (wave_m * C::WM + i * 16) * BK, off0, off1); };
+  auto b_frag = [&](const uint8_t* stage, int j) {
+    return frag(stage + kABytes + (wave_n * C::WN + j * 16) * BK, off0, off1);
+  };
+
+#pragma unroll
+  for (int q = 0; q < kParts; ++q) part(q, 0);
+  advance();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kParts; ++q) part(q, 1);
+  advance();
+
+  // Weight fragments are read kBAhead columns before their MFMAs (one column
+  // for WGRAD, whose column scales take the registers). bw[0] is the current
+  // column's, bw[q] the one q columns on; the barrier precedes column kBarCol,
+  // the first whose look-ahead read falls into the next step's stage.
+  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : 2;
+  constexpr int kBarCol = C::TN - kBAhead;
+  v8i bw[kBAhead + 1];
+#pragma unroll
+  for (int q = 0; q < kBAhead; ++q) bw[q] = b_frag(smem, q);
+  v8i af[C::TM];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) af[i] = a_frag(smem, i);
+  float sc[C::TM], scp[C::TM], scn[C::TM];
+  read_scales(smem, sc);
+
+  v4f acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // MFMA results waiting to be folded: the result of the chunk's t-th MFMA
+  // (t = j * TM + i) sits in pend[t % 4] until it is folded kLag MFMAs later,
+  // so a fold never waits for the matrix core. The last kLag results of a
+  // chunk are folded during the next chunk's first MFMAs with that chunk's
+  // scales (scp), or before the epilogue at the end of a tile.
+  constexpr int kNT = C::TM * C::TN;
+  constexpr int kLag = 3;
+  static_assert(kNT % 4 == 0 && kNT > kLag, "result ring");
+  static_assert(kLag <= C::TM, "a column's folds finish within the next column");
+  v4f pend[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pend[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
+  v4f sbj[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  // Step s: weight columns 0 .. TN-2 from stage s % 2 with fragments already in
+  // registers; then the barrier (every wave has read all of stage s % 2, and
+  // step s + 1 has landed in the other stage), the DMA of step s + 2 into
+  // stage s % 2, and the last column's MFMAs while the fragments of step s + 1
+  // are read (each activation fragment right after its last use).
+  int s = 0;
+#pragma clang loop unroll(disable)
+  for (int tk = 0; tk < my_tiles; ++tk) {
+#pragma clang loop unroll(disable)
+    for (int c = 0; c < nc; ++c, ++s) {
+      const uint8_t* stage = smem + (s & 1) * kStage;
+      const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        if (j == kBarCol) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          read_scales(nstage, scn);
+        }
+        bw[kBAhead] = j + kBAhead < C::TN ? b_frag(stage, j + kBAhead) : b_frag(nstage, j + kBAhead - C::TN);
+        // WGRAD column scales of column j (the last column's are read before
+        // the barrier, below: after it the stage is being refilled)
+        if constexpr (KIND == KIND_WGRAD) {
+          if (j + 1 < C::TN) sbj[j & 1] = wgrad_col_scales(stage, j);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          const int t = j * C::TM + i;
+          pend[t % 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], zero, 0, 0, 0, 0, 0, 0);
+          if (t >= kLag) {
+            const int u = t - kLag;
+            fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], sc[u % C::TM], sbj[(u / C::TM) & 1]);
+          } else {
+            const int u = t - kLag + kNT;   // previous chunk, last column
+            fold<KIND>(acc[u % C::TM][C::TN - 1], pend[u % 4], scp[u % C::TM], sbj[(C::TN - 1) & 1]);
+          }
+          if (j + 1 == C::TN) af[i] = a_frag(nstage, i);
+          // column TN-2's last MFMA: the folds of column TN-3 are done, so its
+          // slot takes the last column's scales
+          if constexpr (KIND == KIND_WGRAD) {
+            if (j + 2 == C::TN && i + 1 == C::TM) sbj[(j + 1) & 1] = wgrad_col_scales(stage, j + 1);
+          }
+          // the cursor's step into stage s % 2 (free since the barrier): one
+          // load per MFMA after it (two at the first), then the cursor moves on
+          {
+            constexpr int kFirst = C::TM * kBarCol;
+            constexpr int kExtra = kParts - (kNT - kFirst);   // loads doubled up at the first slot
+            static_assert(kExtra >= 0 && kExtra < kParts, "load slots after the barrier");
+            if (t == kFirst) {
+#pragma unroll
+              for (int q = 0; q <= kExtra; ++q) part(q, s & 1);
+            } else if (t > kFirst) {
+              part(t - kFirst + kExtra, s & 1);
+            }
+            if (t + 1 == kNT) advance();
+          }
+          // keep this order: one MFMA, the fold of the result kLag MFMAs old,
+          // then the reads due here (no result waits for the matrix core, and
+          // MFMA results never pile up in registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kBAhead; ++q) bw[q] = bw[q + 1];
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) { scp[i] = sc[i]; sc[i] = scn[i]; }
     }
 
-    // ---- tile done: last column's fold, epilogue, next tile ----------------
-    if constexpr (Carry<KIND, C>::kUsed) {
+    // ---- tile done: remaining folds (scales of the tile's last chunk, now in
+    // scp), epilogue; the next tile's first folds then add zeros ------------
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        fold<KIND, C>(acc[i][C::TN - 1], carry.p[i], carry.sc[i], carry.sbj);
-        carry.p[i] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    for (int u = kNT - kLag; u < kNT; ++u)
+      fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], sbj[(u / C::TM) & 1]);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
+    const Tile cur = make_tile<GROUPED>(p, g, start + local + nper * tk);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       const int64_t row = cur.m0 + wave_m * C::WM + i * 16 + l16;
@@ -406,10 +470,10 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
         acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
     }
-    c = 0;
-    ++tk;
-    cur = nxt;
   }
+  // the repeated loads after the last step must land before the workgroup's
+  // LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda, const float* sa,
