@@ -43,6 +43,8 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kABytes = BM * BK;
@@ -53,7 +55,7 @@ constexpr int kStage = kSbOff + BN * 4;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-template <int WAVES_M, int WAVES_N>
+template <int WAVES_M, int WAVES_N, int LOADERS>
 struct Cfg {
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
@@ -61,7 +63,8 @@ struct Cfg {
   static constexpr int WN = BN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
-  static constexpr int kRowsPerRound = 8 * kWaves;        // one dwordx4 DMA per wave covers 8 rows
+  static constexpr int kLoaders = LOADERS;                 // waves that issue the operand loads
+  static constexpr int kRowsPerRound = 8 * kLoaders;       // one dwordx4 DMA per wave covers 8 rows
   static constexpr int kRounds = BM / kRowsPerRound;
   static_assert(WN == 128, "one weight block column per wave");
   static_assert(BM == BN && BM % kRowsPerRound == 0, "tile / wave grid");
@@ -187,9 +190,9 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g,
 // that XCD's workgroups, so blocks resident on one XCD (one L2) work on
 // neighbouring tiles. The first chunk of the next tile is fetched during the
 // current tile's last chunk, so the pipeline fills once per workgroup.
-template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
-  using C = Cfg<WAVES_M, WAVES_N>;
+template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N, int LOADERS>
+__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
+  using C = Cfg<WAVES_M, WAVES_N, LOADERS>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -211,27 +214,26 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const int nc = (int)(p.k / BK);
   const int total = my_tiles * nc;
 
-  // ---- per-lane load offsets of one tile (global -> LDS) --------------------
-  // Round i of wave w covers tile rows [i * kRowsPerRound + 8 w, +8); lane ln
-  // fills row ... + ln / 8, physical slot ln % 8, i.e. logical slot
-  // (ln % 8) ^ swz(row). Offsets are 32-bit relative to the tile's first
-  // row (the host checks that 256 rows of either operand span less than 2 GiB);
-  // rows past the end of the operand repeat its last row (their results are
-  // never stored). Scales: waves 0-3 bring 64 activation scales each; waves
-  // 4-7 bring 64 column scales each (WGRAD) or the tile's two weight block
-  // scales (lane 0 the first block, the other lanes the second, which is the
-  // first again when the tile has only one; waves 5-7 write unused copies).
-  uint32_t a_off[C::kRounds], b_off[C::kRounds], s_off;
+  // ---- global -> LDS load geometry -----------------------------------------
+  // Loader wave w (w < kLoaders) fills, in round i, tile rows
+  // i * kRowsPerRound + 8 w + ln / 8 (lane ln), 16 bytes at physical slot
+  // ln % 8, i.e. logical slot (ln % 8) ^ swz(row); with an even number of
+  // loaders swz(row) = (ln / 8) ^ (w & 1) in every round, so a lane's slot is
+  // fixed and only its row moves. The lane's byte offset from the tile's
+  // first row is computed per load; rows past the end of the operand repeat
+  // its last row (their results are never stored). Offsets are 32-bit (the
+  // host checks that 256 rows of either operand span less than 2 GiB).
+  // Scales: waves 0-3 bring 64 activation scales each; waves 4-7 bring 64
+  // column scales each (WGRAD), or wave 4 brings the tile's two weight block
+  // scales (lane 0 the first block, lane 1 the second, which is the first
+  // again when the tile has only one).
+  static_assert(C::kLoaders % 2 == 0, "fixed slot per lane");
+  const uint32_t lrow = 8 * wave + (lane >> 3);
+  const uint32_t g16 = (uint32_t)(((lane & 7) ^ (lane >> 3) ^ (wave & 1)) * 16);
+  uint32_t s_off = 0, a_last = 0, b_last = 0;
   auto set_offsets = [&](const Tile& t) {
-#pragma unroll
-    for (int i = 0; i < C::kRounds; ++i) {
-      const int row = i * C::kRowsPerRound + 8 * wave + (lane >> 3);
-      const int gslot = (lane & 7) ^ swz(row);
-      const int64_t ar = min(t.m0 + row, t.m_end - 1) - t.m0;
-      const int64_t br = min(t.n0 + row, t.n_end - 1) - t.n0;
-      a_off[i] = (uint32_t)(ar * p.lda + gslot * 16);
-      b_off[i] = (uint32_t)(br * p.ldb + gslot * 16);
-    }
+    a_last = (uint32_t)(t.m_end - t.m0 - 1);
+    b_last = (uint32_t)(t.n_end - t.n0 - 1);
     const int q4 = wave & 3;
     if (wave < 4) {
       s_off = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
@@ -243,6 +245,9 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
       const int64_t bsel = lane < 1 ? 0 : blk1;
       s_off = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
     }
+  };
+  auto row_off = [&](int i, uint32_t last, uint32_t ld) {
+    return min((uint32_t)(i * C::kRowsPerRound) + lrow, last) * ld + g16;
   };
 
   // ---- global -> LDS cursor: runs two steps ahead of the MFMAs -------------
@@ -288,12 +293,20 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   cursor_tile();
   auto part = [&](int q, int st) {
     const uint32_t base = lds_addr(smem) + (uint32_t)(st * kStage);
-    if (q < C::kRounds)
-      dma16(d_ak, a_off[q], base + (q * C::kRowsPerRound + 8 * wave) * BK);
-    else if (q < 2 * C::kRounds)
-      dma16(d_bk, b_off[q - C::kRounds], base + kABytes + ((q - C::kRounds) * C::kRowsPerRound + 8 * wave) * BK);
-    else
+    if (q < 2 * C::kRounds) {
+      if (wave >= C::kLoaders) return;
+      if (q < C::kRounds)
+        dma16(d_ak, row_off(q, a_last, (uint32_t)p.lda), base + (q * C::kRowsPerRound + 8 * wave) * BK);
+      else
+        dma16(d_bk, row_off(q - C::kRounds, b_last, (uint32_t)p.ldb),
+              base + kABytes + ((q - C::kRounds) * C::kRowsPerRound + 8 * wave) * BK);
+    } else if (wave < 4 || KIND == KIND_WGRAD) {
       dma4(uniform_ptr(d_sk), s_off, base + (wave < 4 ? kSaOff : kSbOff) + 256 * (wave & 3));
+    } else if (wave == 4) {
+      // FPROP / DGRAD: the tile's two weight block scales; a load's cost
+      // follows its active lanes, so only two lanes take part
+      if (lane < 2) dma4(uniform_ptr(d_sk), s_off, base + kSbOff);
+    }
   };
 
   // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
@@ -412,17 +425,16 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
           if constexpr (KIND == KIND_WGRAD) {
             if (j + 2 == C::TN && i + 1 == C::TM) sbj[(j + 1) & 1] = wgrad_col_scales(stage, j + 1);
           }
-          // the cursor's step into stage s % 2 (free since the barrier): one
-          // load per MFMA after it (two at the first), then the cursor moves on
+          // the cursor's step into stage s % 2 (free since the barrier): its
+          // loads spread evenly over the MFMAs after the barrier, then the
+          // cursor moves on
           {
             constexpr int kFirst = C::TM * kBarCol;
-            constexpr int kExtra = kParts - (kNT - kFirst);   // loads doubled up at the first slot
-            static_assert(kExtra >= 0 && kExtra < kParts, "load slots after the barrier");
-            if (t == kFirst) {
+            constexpr int kSlots = kNT - kFirst;
+            if (t >= kFirst) {
 #pragma unroll
-              for (int q = 0; q <= kExtra; ++q) part(q, s & 1);
-            } else if (t > kFirst) {
-              part(t - kFirst + kExtra, s & 1);
+              for (int q = 0; q < kParts; ++q)
+                if (q * kSlots / kParts == t - kFirst) part(q, s & 1);
             }
             if (t + 1 == kNT) advance();
           }
@@ -457,14 +469,15 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
             float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
             *reinterpret_cast<v4f*>(o) = acc[i][j];
           } else {
-            uint32_t h[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t u = __float_as_uint(acc[i][j][r]);
-              h[r] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // round to nearest even (finite)
-            }
+            // v_cvt_pk_bf16_f32 rounds to nearest even (equal to the integer
+            // rounding on every finite fp32, checked exhaustively on gfx950)
+            const bf16x2 lo = __builtin_convertvector((f32x2){acc[i][j][0], acc[i][j][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2){acc[i][j][2], acc[i][j][3]}, bf16x2);
+            uint2 packed;
+            __builtin_memcpy(&packed.x, &lo, 4);
+            __builtin_memcpy(&packed.y, &hi, 4);
             uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
-            *reinterpret_cast<uint2*>(o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2*>(o) = packed;
           }
         }
         acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -491,7 +504,11 @@ GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t ld
 
 constexpr int kWM = 4;   // 4 x 2 waves of 64 x 128: the accumulator must stay within the
 constexpr int kWN = 2;   // 256 VGPRs the VALU can address, with room for fragments
-constexpr int kBlock = Cfg<kWM, kWN>::kThreads;
+#ifndef FP8BQ_LOADERS
+#define FP8BQ_LOADERS 8
+#endif
+constexpr int kLd = FP8BQ_LOADERS;   // waves issuing the operand loads
+constexpr int kBlock = Cfg<kWM, kWN, kLd>::kThreads;
 
 // One workgroup per CU (the LDS stages take most of a CU's 160 KB): as many
 // workgroups as CUs, or as tiles when there are fewer tiles.
@@ -515,9 +532,9 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
   g.groups = 0;
   const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
   switch (kind) {
-    case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN>), grid, block, 0, st, p, g); break;
-    case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN>), grid, block, 0, st, p, g); break;
-    default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false, kWM, kWN>), grid, block, 0, st, p, g); break;
+    case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
+    case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
+    default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
   }
   return hipGetLastError();
 }
@@ -540,7 +557,7 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, in
   p.tiles_m = tiles;
   if (tiles == 0) return hipSuccess;   // every group empty: nothing to compute
   const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
-  hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN>), grid, block, 0, st, p, g);
+  hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN, kLd>), grid, block, 0, st, p, g);
   return hipGetLastError();
 }
 
