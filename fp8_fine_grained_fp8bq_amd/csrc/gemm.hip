@@ -350,7 +350,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
   // for WGRAD, whose column scales take the registers). bw[0] is the current
   // column's, bw[q] the one q columns on; the barrier precedes column kBarCol,
   // the first whose look-ahead read falls into the next step's stage.
-  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : 2;
+  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : 3;
   constexpr int kBarCol = C::TN - kBAhead;
   v8i bw[kBAhead + 1];
 #pragma unroll
