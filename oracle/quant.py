@@ -24,6 +24,16 @@ Readings where the pages leave a step open:
 * A tile whose absmax is zero gets s = 0 and codes +0 / -0 by the sign of x.
 * Inputs are bf16 bit patterns (uint16) and must be finite.
 
+Power-of-two scales (scale_mode="pow2"): the report (section 3.3.3,
+"low-precision storage and communication") gives some activations scaling
+factors that are integral powers of 2 (the inputs of the Linear after
+attention, the activations dispatched to the MoE up-projection). Reading: s is
+the smallest power of two with absmax / s <= 448, i.e. s = 2^k with
+k = ceil(log2(absmax / 448)), so nothing saturates; k is kept within
+[-127, 127] (the range of the E8M0 exponent byte a scaled matrix instruction
+takes) and an all-zero group gets s = 2^-127. Then q = E4M3(x * 2^-k), where
+the product is exact, so there is one rounding instead of two.
+
 Scale layout here is the natural one: s[r, c] for row r and 128-column chunk c.
 
 Pinned by: tests/test_oracle_quant.py -- every tile's absmax element lands on
@@ -48,11 +58,42 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32)
 
 
-def _quant_groups(xg: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+K_MIN, K_MAX = -127, 127   # exponent range of a power-of-two scale
+
+
+def pow2_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer k with amax <= 448 * 2^k, clamped to [K_MIN, K_MAX];
+    K_MIN for amax = 0. Found by search from a float estimate and corrected in
+    exact arithmetic (448 * 2^k and amax are exact in float64)."""
+    a = np.asarray(amax, dtype=np.float64)
+    pos = a > 0
+    est = np.zeros(a.shape, dtype=np.int64)
+    est[pos] = np.ceil(np.log2(a[pos] / 448.0)).astype(np.int64)
+    k = est.copy()
+    for _ in range(4):   # the estimate is off by at most one either way
+        k = np.where(pos & (a > 448.0 * np.ldexp(1.0, k)), k + 1, k)
+        k = np.where(pos & (a <= 448.0 * np.ldexp(1.0, k - 1)), k - 1, k)
+    k = np.where(pos, k, K_MIN)
+    return np.clip(k, K_MIN, K_MAX)
+
+
+def _quant_groups_pow2(xg: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Power-of-two scales: s = 2^k as above, q = E4M3(x * 2^-k) (exact product)."""
+    amax = np.max(np.abs(xg), axis=-1)
+    k = pow2_exponent(amax)
+    v = xg.astype(np.float64) * np.ldexp(1.0, -k)[..., None]      # exact
+    q = e4m3.encode(v)
+    return q, np.ldexp(np.float32(1.0), k.astype(np.int32)).astype(np.float32)
+
+
+def _quant_groups(xg: np.ndarray, scale_mode: str = "exact") -> tuple[np.ndarray, np.ndarray]:
     """Quantise groups laid out along the last axis of `xg` (float32).
 
     Returns (codes uint8 with the shape of xg, scales float32 of xg.shape[:-1]).
     """
+    if scale_mode == "pow2":
+        return _quant_groups_pow2(xg)
+    assert scale_mode == "exact", scale_mode
     amax = np.max(np.abs(xg), axis=-1)                         # exact
     s = (amax.astype(np.float32) / F_MAX).astype(np.float32)   # fl32(amax / 448)
     zero = s == 0
@@ -66,7 +107,7 @@ def _quant_groups(xg: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
-def quant_act_1x128(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_act_1x128(x_bits: np.ndarray, scale_mode: str = "exact") -> tuple[np.ndarray, np.ndarray]:
     """1x128 tiles along the columns of a bf16 matrix x[rows, cols].
 
     Returns q uint8 [rows, cols] and s float32 [rows, cols // 128].
@@ -74,11 +115,11 @@ def quant_act_1x128(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     x = bf16_bits_to_f32(x_bits)
     rows, cols = x.shape
     assert cols % TILE == 0, "columns must be a multiple of 128"
-    q, s = _quant_groups(x.reshape(rows, cols // TILE, TILE))
+    q, s = _quant_groups(x.reshape(rows, cols // TILE, TILE), scale_mode)
     return q.reshape(rows, cols), s
 
 
-def quant_act_128x1(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_act_128x1(x_bits: np.ndarray, scale_mode: str = "exact") -> tuple[np.ndarray, np.ndarray]:
     """128x1 tiles (128 consecutive rows of one column) of x[rows, cols].
 
     The result is stored transposed so that the grouped dimension is
@@ -87,10 +128,10 @@ def quant_act_128x1(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     assert x_bits.shape[0] % TILE == 0, "rows must be a multiple of 128"
-    return quant_act_1x128(np.ascontiguousarray(x_bits.T))
+    return quant_act_1x128(np.ascontiguousarray(x_bits.T), scale_mode)
 
 
-def quant_w_128x128(w_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_w_128x128(w_bits: np.ndarray, scale_mode: str = "exact") -> tuple[np.ndarray, np.ndarray]:
     """128x128 blocks of a bf16 weight w[n, k].
 
     Returns q uint8 [n, k] and s float32 [n // 128, k // 128].
@@ -99,7 +140,7 @@ def quant_w_128x128(w_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     n, k = w.shape
     assert n % TILE == 0 and k % TILE == 0, "weight dims must be multiples of 128"
     blocks = w.reshape(n // TILE, TILE, k // TILE, TILE).transpose(0, 2, 1, 3)
-    q, s = _quant_groups(blocks.reshape(n // TILE, k // TILE, TILE * TILE))
+    q, s = _quant_groups(blocks.reshape(n // TILE, k // TILE, TILE * TILE), scale_mode)
     q = q.reshape(n // TILE, k // TILE, TILE, TILE).transpose(0, 2, 1, 3).reshape(n, k)
     return np.ascontiguousarray(q), s
 

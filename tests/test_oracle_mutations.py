@@ -81,7 +81,7 @@ def test_division_precision_reading_is_observable(monkeypatch):
     # computing x / s in float64 (no binary32 rounding of the quotient) is a different reading
     orig = quant._quant_groups
 
-    def groups64(xg):
+    def groups64(xg, scale_mode="exact"):
         amax = np.max(np.abs(xg), axis=-1)
         s = (amax.astype(np.float32) / quant.F_MAX).astype(np.float32)
         v = xg.astype(np.float64) / np.where(s == 0, 1, s)[..., None].astype(np.float64)
