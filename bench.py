@@ -138,7 +138,7 @@ def main():
         fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE, xq.data_ptr(), K, xs.data_ptr(), M, sp)
 
     def quant_w():
-        fb.fp8bq_quant_w_128x128(w.data_ptr(), N, K, K, wq.data_ptr(), K, ws.data_ptr(), K // 128, None, N, sp)
+        fb.fp8bq_quant_w_128x128(w.data_ptr(), N, K, K, wq.data_ptr(), K, ws.data_ptr(), K // 128, None, N, 0, sp)
 
     def gemm():
         fb.fp8bq_gemm(fb.FPROP, M, N, K, xq.data_ptr(), K, xs.data_ptr(), M, wq.data_ptr(), K,

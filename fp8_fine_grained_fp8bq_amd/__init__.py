@@ -29,6 +29,7 @@ OK, E_INVAL, E_SHAPE, E_ALIGN, E_DEVICE, E_HIP = range(6)
 STATUS_NAMES = {0: "OK", 1: "E_INVAL", 2: "E_SHAPE", 3: "E_ALIGN", 4: "E_DEVICE", 5: "E_HIP"}
 FPROP, DGRAD, WGRAD = 0, 1, 2
 ACT_ROWWISE, ACT_COLWISE = 0, 1
+SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm",
            "fp8bq_last_error", "fp8bq_version")
@@ -53,10 +54,10 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, fp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
         L.fp8bq_quant_act_1x128.argtypes = [vp, i64, i64, i64, i32, vp, i64, fp, i64, vp]
-        L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, vp]
+        L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
         L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
-                                         vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
+                                         vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm"):
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
@@ -82,9 +83,9 @@ def fp8bq_quant_act_1x128(x, rows, cols, ldx, mode, q, ldq, s, lds, stream=0):
                   lib().fp8bq_quant_act_1x128(x, rows, cols, ldx, mode, q, ldq, s, lds, stream))
 
 
-def fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, stream=0):
+def fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, flags=0, stream=0):
     return _check("fp8bq_quant_w_128x128",
-                  lib().fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, stream))
+                  lib().fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, flags, stream))
 
 
 def fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
@@ -92,12 +93,13 @@ def fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream
                   lib().fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream))
 
 
-def fp8bq_grouped_gemm(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
+def fp8bq_grouped_gemm(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, flags=0,
+                       stream=0):
     """`row_off` is a sequence of groups + 1 ints (host memory)."""
     arr = (ctypes.c_int64 * (groups + 1))(*[int(v) for v in row_off]) if row_off is not None else None
     return _check("fp8bq_grouped_gemm",
                   lib().fp8bq_grouped_gemm(groups, arr, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb,
-                                           out, ldo, stream))
+                                           out, ldo, flags, stream))
 
 
 def version() -> str:
@@ -122,11 +124,12 @@ def _bf16_2d(t, name):
 
 def quant_act_1x128(x, mode: int = ACT_ROWWISE):
     """x bf16 [rows, cols] -> (q uint8, s float32) as laid out by the C ABI:
-    ROWWISE q [rows, cols], s [cols/128, rows]; COLWISE q [cols, rows], s [rows/128, cols]."""
+    ROWWISE q [rows, cols], s [cols/128, rows]; COLWISE q [cols, rows], s [rows/128, cols].
+    `mode` may include SCALE_POW2 (power-of-two scales)."""
     import torch
     _bf16_2d(x, "x")
     rows, cols = x.shape
-    if mode == ACT_ROWWISE:
+    if (mode & ~SCALE_POW2) == ACT_ROWWISE:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
         s = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
         ldq, lds = cols, rows
@@ -139,8 +142,9 @@ def quant_act_1x128(x, mode: int = ACT_ROWWISE):
     return q, s
 
 
-def quant_w_128x128(w, transposed_copy: bool = False):
-    """w bf16 [n, k] -> (q uint8 [n, k], s float32 [n/128, k/128], qt uint8 [k, n] or None)."""
+def quant_w_128x128(w, transposed_copy: bool = False, pow2: bool = False):
+    """w bf16 [n, k] -> (q uint8 [n, k], s float32 [n/128, k/128], qt uint8 [k, n] or None);
+    pow2 selects power-of-two scales."""
     import torch
     _bf16_2d(w, "w")
     n, k = w.shape
@@ -148,18 +152,19 @@ def quant_w_128x128(w, transposed_copy: bool = False):
     s = torch.empty((n // 128, k // 128), dtype=torch.float32, device=w.device)
     qt = torch.empty((k, n), dtype=torch.uint8, device=w.device) if transposed_copy else None
     fp8bq_quant_w_128x128(w.data_ptr(), n, k, w.stride(0), q.data_ptr(), k, s.data_ptr(), k // 128,
-                          qt.data_ptr() if qt is not None else None, n, _stream(w))
+                          qt.data_ptr() if qt is not None else None, n, SCALE_POW2 if pow2 else 0, _stream(w))
     return q, s, qt
 
 
 def gemm(op: int, a, sa, b, sb, out=None):
     """a uint8 [m, k] with chunk-major scales sa [k/128, >=m]; b uint8 [n, k] with
-    sb laid out per `op` (see include/fp8bq.h). Returns out (bf16 or fp32) [m, n]."""
+    sb laid out per `op` (see include/fp8bq.h); `op` may include SCALE_POW2. Returns out
+    (bf16 or fp32) [m, n]."""
     import torch
     m, k = a.shape
     n = b.shape[0]
     if out is None:
-        dt = torch.float32 if op == WGRAD else torch.bfloat16
+        dt = torch.float32 if (op & ~SCALE_POW2) == WGRAD else torch.bfloat16
         out = torch.empty((m, n), dtype=dt, device=a.device)
     fp8bq_gemm(op, m, n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
                b.data_ptr(), b.stride(0), sb.data_ptr(), sb.stride(0), out.data_ptr(), out.stride(0),
@@ -167,9 +172,10 @@ def gemm(op: int, a, sa, b, sb, out=None):
     return out
 
 
-def grouped_gemm(row_off, a, sa, b, sb, out=None):
+def grouped_gemm(row_off, a, sa, b, sb, out=None, pow2: bool = False):
     """row_off: host sequence of G + 1 row offsets (multiples of 128); a uint8 [m, k];
-    sa [k/128, >=m]; b uint8 [G, n, k]; sb float32 [G, n/128, k/128]. Returns bf16 [m, n]."""
+    sa [k/128, >=m]; b uint8 [G, n, k]; sb float32 [G, n/128, k/128]. Returns bf16 [m, n].
+    pow2: power-of-two scales applied by the matrix instruction."""
     import torch
     G, n, k = b.shape
     m = a.shape[0]
@@ -177,5 +183,5 @@ def grouped_gemm(row_off, a, sa, b, sb, out=None):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
     fp8bq_grouped_gemm(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
                        b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
-                       out.stride(0), _stream(a))
+                       out.stride(0), SCALE_POW2 if pow2 else 0, _stream(a))
     return out

@@ -67,12 +67,14 @@ const char* fp8bq_last_error(void) { return g_err; }
 
 const char* fp8bq_version(void) { return "fp8bq 0.1 (gfx950)"; }
 
-int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode,
+int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, int mode_flags,
                           void* q, int64_t ldq, float* s, int64_t lds, void* stream) {
   if (!x || !q || !s) return fail(FP8BQ_E_INVAL, "quant_act: null pointer");
   if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "quant_act: rows and cols must be positive");
+  const bool pow2 = (mode_flags & FP8BQ_SCALE_POW2) != 0;
+  const int mode = mode_flags & ~FP8BQ_SCALE_POW2;
   if (mode != FP8BQ_ACT_ROWWISE && mode != FP8BQ_ACT_COLWISE)
-    return fail(FP8BQ_E_INVAL, "quant_act: mode must be ROWWISE (0) or COLWISE (1), got %d", mode);
+    return fail(FP8BQ_E_INVAL, "quant_act: mode must be ROWWISE (0) or COLWISE (1), optionally | SCALE_POW2, got %d", mode_flags);
   if (ldx < cols) return fail(FP8BQ_E_INVAL, "quant_act: ldx (%lld) < cols (%lld)", (long long)ldx, (long long)cols);
   if (cols % 128) return fail(FP8BQ_E_SHAPE, "quant_act: cols (%lld) must be a multiple of 128", (long long)cols);
   if (mode == FP8BQ_ACT_ROWWISE) {
@@ -92,14 +94,15 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
   hipStream_t str = reinterpret_cast<hipStream_t>(stream);
   if (mode == FP8BQ_ACT_ROWWISE)
     return launched(fp8bq::launch_quant_act_rows(static_cast<const uint16_t*>(x), rows, cols, ldx,
-                                                 static_cast<uint8_t*>(q), ldq, s, lds, str), "quant_act");
+                                                 static_cast<uint8_t*>(q), ldq, s, lds, pow2, str), "quant_act");
   return launched(fp8bq::launch_quant_act_cols(static_cast<const uint16_t*>(x), rows, cols, ldx,
-                                               static_cast<uint8_t*>(q), ldq, s, lds, str), "quant_act");
+                                               static_cast<uint8_t*>(q), ldq, s, lds, pow2, str), "quant_act");
 }
 
 int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
-                          float* s, int64_t lds, void* qt, int64_t ldqt, void* stream) {
+                          float* s, int64_t lds, void* qt, int64_t ldqt, int flags, void* stream) {
   if (!w || !q || !s) return fail(FP8BQ_E_INVAL, "quant_w: null pointer");
+  if (flags & ~FP8BQ_SCALE_POW2) return fail(FP8BQ_E_INVAL, "quant_w: unknown flags %d", flags);
   if (n <= 0 || k <= 0) return fail(FP8BQ_E_INVAL, "quant_w: n and k must be positive");
   if (ldw < k || ldq < k) return fail(FP8BQ_E_INVAL, "quant_w: ldw and ldq must be >= k");
   if (lds < k / 128) return fail(FP8BQ_E_INVAL, "quant_w: lds must be >= k / 128");
@@ -113,6 +116,7 @@ int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void
   if (int st = check_device()) return st;
   return launched(fp8bq::launch_quant_w(static_cast<const uint16_t*>(w), n, k, ldw, static_cast<uint8_t*>(q),
                                         ldq, s, lds, static_cast<uint8_t*>(qt), ldqt,
+                                        (flags & FP8BQ_SCALE_POW2) != 0,
                                         reinterpret_cast<hipStream_t>(stream)), "quant_w");
 }
 
@@ -138,11 +142,14 @@ int check_gemm_common(const char* who, int64_t m, int64_t n, int64_t k, const vo
 
 }  // namespace
 
-int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* sa,
+int fp8bq_gemm(int op_flags, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, const float* sa,
                int64_t ldsa, const void* b, int64_t ldb, const float* sb, int64_t ldsb, void* out,
                int64_t ldo, void* stream) {
+  const bool pow2 = (op_flags & FP8BQ_SCALE_POW2) != 0;
+  const int op = op_flags & ~FP8BQ_SCALE_POW2;
   if (op != FP8BQ_FPROP && op != FP8BQ_DGRAD && op != FP8BQ_WGRAD)
-    return fail(FP8BQ_E_INVAL, "gemm: op must be FPROP (0), DGRAD (1) or WGRAD (2), got %d", op);
+    return fail(FP8BQ_E_INVAL, "gemm: op must be FPROP (0), DGRAD (1) or WGRAD (2), optionally | SCALE_POW2, got %d",
+                op_flags);
   if (int st = check_gemm_common("gemm", m, n, k, a, lda, sa, b, ldb, sb, out, ldo, op == FP8BQ_WGRAD ? 4 : 2))
     return st;
   if (ldsa < m) return fail(FP8BQ_E_INVAL, "gemm: ldsa must be >= m");
@@ -151,13 +158,14 @@ int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k, const void* a, int64_t l
   if (op == FP8BQ_WGRAD && ldsb < n) return fail(FP8BQ_E_INVAL, "gemm: WGRAD ldsb must be >= n");
   if (int st = check_device()) return st;
   return launched(fp8bq::launch_gemm(op, m, n, k, static_cast<const uint8_t*>(a), lda, sa, ldsa,
-                                     static_cast<const uint8_t*>(b), ldb, sb, ldsb, out, ldo,
+                                     static_cast<const uint8_t*>(b), ldb, sb, ldsb, out, ldo, pow2,
                                      reinterpret_cast<hipStream_t>(stream)), "gemm");
 }
 
 int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
                        int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
-                       const float* sb, int64_t ldsb, void* out, int64_t ldo, void* stream) {
+                       const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags, void* stream) {
+  if (flags & ~FP8BQ_SCALE_POW2) return fail(FP8BQ_E_INVAL, "grouped_gemm: unknown flags %d", flags);
   if (groups < 1 || groups > fp8bq::kMaxGroups)
     return fail(FP8BQ_E_INVAL, "grouped_gemm: groups must be in [1, %d], got %d", fp8bq::kMaxGroups, groups);
   if (!row_off) return fail(FP8BQ_E_INVAL, "grouped_gemm: null row_off");
@@ -176,7 +184,8 @@ int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_
   if (m == 0) return FP8BQ_OK;
   return launched(fp8bq::launch_grouped_gemm(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda, sa, ldsa,
                                              static_cast<const uint8_t*>(b), ldb, sb, ldsb,
-                                             static_cast<uint16_t*>(out), ldo, reinterpret_cast<hipStream_t>(stream)),
+                                             static_cast<uint16_t*>(out), ldo, (flags & FP8BQ_SCALE_POW2) != 0,
+                                             reinterpret_cast<hipStream_t>(stream)),
                   "grouped_gemm");
 }
 

@@ -55,7 +55,7 @@ constexpr int kStage = kSbOff + BN * 4;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-template <int WAVES_M, int WAVES_N, int LOADERS>
+template <int WAVES_M, int WAVES_N>
 struct Cfg {
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
@@ -63,12 +63,8 @@ struct Cfg {
   static constexpr int WN = BN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
-  static constexpr int kLoaders = LOADERS;                 // waves that issue the operand loads
-  static constexpr int kRowsPerRound = 8 * kLoaders;       // one dwordx4 DMA per wave covers 8 rows
-  static constexpr int kRounds = BM / kRowsPerRound;
   static_assert(WN == 128, "one weight block column per wave");
-  static_assert(BM == BN && BM % kRowsPerRound == 0, "tile / wave grid");
-  static_assert(kWaves == 8, "scale loaders: four 64-lane dword DMAs per side");
+  static_assert(BM == BN, "square workgroup tile");
 };
 
 struct GemmArgs {
@@ -184,15 +180,163 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g,
   return t;
 }
 
-// Persistent kernel: each workgroup owns one CU and walks a strided list of
-// output tiles. Workgroup w runs on XCD w % 8 (hardware round-robin); the
-// tiles of XCD x are a contiguous range of the grouped walk, shared out among
-// that XCD's workgroups, so blocks resident on one XCD (one L2) work on
-// neighbouring tiles. The first chunk of the next tile is fetched during the
-// current tile's last chunk, so the pipeline fills once per workgroup.
+// This workgroup's share of the persistent tile walk. Workgroup w runs on XCD
+// w % 8 (hardware round-robin); the tiles of XCD x are a contiguous range of
+// the grouped walk, shared out among that XCD's workgroups, so blocks resident
+// on one XCD (one L2) work on neighbouring tiles. Its tiles are logical
+// indices start + local + nper * t, t = 0 .. my_tiles - 1.
+struct Walk {
+  int start, local, nper, my_tiles, nc, total;
+};
+
+__device__ __forceinline__ Walk make_walk(const GemmArgs& p) {
+  Walk wk;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int T = p.tiles_m * p.tiles_n;
+  const int x = w % kXcds;
+  wk.local = w / kXcds;
+  wk.nper = G / kXcds + (x < G % kXcds ? 1 : 0);
+  const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
+  wk.start = x * (T / kXcds) + min(x, T % kXcds);
+  wk.my_tiles = wk.local < count ? (count - wk.local + wk.nper - 1) / wk.nper : 0;
+  wk.nc = (int)(p.k / BK);
+  wk.total = wk.my_tiles * wk.nc;
+  return wk;
+}
+
+// ---- global -> LDS loads ----------------------------------------------------
+// Loader wave w (w < LOADERS) fills, in round i, tile rows
+// i * kRowsPerRound + 8 w + ln / 8 (lane ln), 16 bytes at physical slot
+// ln % 8, i.e. logical slot (ln % 8) ^ swz(row); with an even number of
+// loaders swz(row) = (ln / 8) ^ (w & 1) in every round, so a lane's slot is
+// fixed and only its row moves. The lane's byte offset from the tile's first
+// row is computed per load; rows past the end of the operand repeat its last
+// row (their results are never stored). Offsets are 32-bit (the host checks
+// that 256 rows of either operand span less than 2 GiB).
+// Scales are brought by eight "scale waves" of 64 lanes (each real wave plays
+// 8 / WAVES of them): scale waves 0-3 bring 64 activation scales each; 4-7
+// bring 64 column scales each (WGRAD), or scale wave 4 brings the tile's two
+// weight block scales (lane 0 the first block, lane 1 the second, which is the
+// first again when the tile has only one).
+//
+// The cursor (dtk, dc) is the next step to load: step s is chunk s % nc of the
+// workgroup's (s / nc)-th tile and lives in stage s % 2; d_ak, d_bk, d_sk point
+// at its chunk of A, B and the scale vectors. A step goes out as kParts load
+// instructions per wave, part(0 .. kParts-1), and then advance() moves the
+// cursor on. After the last step the cursor stays put: further loads repeat
+// that step into a stage no one reads any more (the kernels wait for them
+// before they end), which keeps every load unconditional.
+template <int KIND, bool GROUPED, int WAVES, int LOADERS>
+struct Loader {
+  static constexpr int kRowsPerRound = 8 * LOADERS;      // one dwordx4 load per wave covers 8 rows
+  static constexpr int kRounds = BM / kRowsPerRound;
+  static constexpr int kScaleWaves = 8 / WAVES;
+  static constexpr int kParts = 2 * kRounds + kScaleWaves;
+  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0, "load rounds");
+  static_assert(WAVES == 4 || WAVES == 8, "scale waves");
+
+  const GemmArgs& p;
+  const GroupArgs& g;
+  const Walk& wk;
+  const uint32_t smem_base;
+  const int wave, lane;
+  const uint32_t lrow, g16;
+  uint32_t a_last = 0, b_last = 0;
+  uint32_t s_off[kScaleWaves];
+  int64_t s_step[kScaleWaves];
+  const float* d_sk[kScaleWaves];
+  const uint8_t* d_ak = nullptr;
+  const uint8_t* d_bk = nullptr;
+  int dtk = 0, dc = 0;
+
+  __device__ __forceinline__ Loader(const GemmArgs& p_, const GroupArgs& g_, const Walk& wk_, uint32_t smem_base_,
+                                    int wave_, int lane_)
+      : p(p_), g(g_), wk(wk_), smem_base(smem_base_), wave(wave_), lane(lane_),
+        lrow(8 * wave_ + (lane_ >> 3)), g16((uint32_t)(((lane_ & 7) ^ (lane_ >> 3) ^ (wave_ & 1)) * 16)) {
+#pragma unroll
+    for (int v = 0; v < kScaleWaves; ++v) {
+      // per-step advance of a scale pointer: activation scales are chunk-major;
+      // FPROP block scales are contiguous along K, DGRAD's and the WGRAD column
+      // scales chunk-major
+      const int sw = wave + v * WAVES;
+      s_step[v] = sw < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
+    }
+    cursor_tile();
+  }
+
+  __device__ __forceinline__ void cursor_tile() {
+    const Tile t = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * dtk);
+    a_last = (uint32_t)(t.m_end - t.m0 - 1);
+    b_last = (uint32_t)(t.n_end - t.n0 - 1);
+    d_ak = p.a + t.m0 * p.lda;
+    d_bk = t.b + t.n0 * p.ldb;
+#pragma unroll
+    for (int v = 0; v < kScaleWaves; ++v) {
+      const int sw = wave + v * WAVES, q4 = sw & 3;
+      if (sw < 4) {
+        s_off[v] = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
+        d_sk[v] = p.sa + t.m0;
+      } else if constexpr (KIND == KIND_WGRAD) {
+        s_off[v] = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
+        d_sk[v] = t.sb + t.n0;
+      } else {
+        const int64_t blk0 = t.n0 / 128;
+        const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
+        const int64_t bsel = lane < 1 ? 0 : blk1;
+        s_off[v] = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
+        d_sk[v] = KIND == KIND_FPROP ? t.sb + blk0 * p.ldsb : t.sb + blk0;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void advance() {
+    if (dc + 1 < wk.nc) {
+      ++dc;
+      d_ak += BK;
+      d_bk += BK;
+#pragma unroll
+      for (int v = 0; v < kScaleWaves; ++v) d_sk[v] += s_step[v];
+    } else if (dtk + 1 < wk.my_tiles) {
+      dc = 0;
+      ++dtk;
+      cursor_tile();
+    }
+  }
+
+  __device__ __forceinline__ uint32_t row_off(int i, uint32_t last, uint32_t ld) const {
+    return min((uint32_t)(i * kRowsPerRound) + lrow, last) * ld + g16;
+  }
+
+  // Load instruction q of the cursor's step into stage st.
+  __device__ __forceinline__ void part(int q, int st) const {
+    const uint32_t base = smem_base + (uint32_t)(st * kStage);
+    if (q < 2 * kRounds) {
+      if (wave >= LOADERS) return;
+      if (q < kRounds)
+        dma16(d_ak, row_off(q, a_last, (uint32_t)p.lda), base + (q * kRowsPerRound + 8 * wave) * BK);
+      else
+        dma16(d_bk, row_off(q - kRounds, b_last, (uint32_t)p.ldb),
+              base + kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
+      return;
+    }
+    const int v = q - 2 * kRounds, sw = wave + v * WAVES;
+    if (sw < 4 || KIND == KIND_WGRAD) {
+      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (sw < 4 ? kSaOff : kSbOff) + 256 * (sw & 3));
+    } else if (sw == 4) {
+      // FPROP / DGRAD: the tile's two weight block scales; a load's cost
+      // follows its active lanes, so only two lanes take part
+      if (lane < 2) dma4(uniform_ptr(d_sk[v]), s_off[v], base + kSbOff);
+    }
+  }
+};
+
+// Persistent kernel with promotion on the VALU: each workgroup owns one CU and
+// walks its tiles (make_walk); the first chunk of the next tile is fetched
+// during the current tile's last chunks, so the pipeline fills once per
+// workgroup.
 template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N, int LOADERS>
-__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
-  using C = Cfg<WAVES_M, WAVES_N, LOADERS>;
+__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
+  using C = Cfg<WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -202,112 +346,11 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
   const int wave_n = wave / WAVES_M;
   const int l16 = lane & 15, lq = lane >> 4;
 
-  // this workgroup's tiles: logical start + local + nper * k, k = 0, 1, ...
-  const int G = gridDim.x, w = blockIdx.x;
-  const int T = p.tiles_m * p.tiles_n;
-  const int x = w % kXcds, local = w / kXcds;
-  const int nper = G / kXcds + (x < G % kXcds ? 1 : 0);
-  const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
-  const int start = x * (T / kXcds) + min(x, T % kXcds);
-  if (local >= count) return;                                  // uniform: no tile for this workgroup
-  const int my_tiles = (count - local + nper - 1) / nper;
-  const int nc = (int)(p.k / BK);
-  const int total = my_tiles * nc;
-
-  // ---- global -> LDS load geometry -----------------------------------------
-  // Loader wave w (w < kLoaders) fills, in round i, tile rows
-  // i * kRowsPerRound + 8 w + ln / 8 (lane ln), 16 bytes at physical slot
-  // ln % 8, i.e. logical slot (ln % 8) ^ swz(row); with an even number of
-  // loaders swz(row) = (ln / 8) ^ (w & 1) in every round, so a lane's slot is
-  // fixed and only its row moves. The lane's byte offset from the tile's
-  // first row is computed per load; rows past the end of the operand repeat
-  // its last row (their results are never stored). Offsets are 32-bit (the
-  // host checks that 256 rows of either operand span less than 2 GiB).
-  // Scales: waves 0-3 bring 64 activation scales each; waves 4-7 bring 64
-  // column scales each (WGRAD), or wave 4 brings the tile's two weight block
-  // scales (lane 0 the first block, lane 1 the second, which is the first
-  // again when the tile has only one).
-  static_assert(C::kLoaders % 2 == 0, "fixed slot per lane");
-  const uint32_t lrow = 8 * wave + (lane >> 3);
-  const uint32_t g16 = (uint32_t)(((lane & 7) ^ (lane >> 3) ^ (wave & 1)) * 16);
-  uint32_t s_off = 0, a_last = 0, b_last = 0;
-  auto set_offsets = [&](const Tile& t) {
-    a_last = (uint32_t)(t.m_end - t.m0 - 1);
-    b_last = (uint32_t)(t.n_end - t.n0 - 1);
-    const int q4 = wave & 3;
-    if (wave < 4) {
-      s_off = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
-    } else if constexpr (KIND == KIND_WGRAD) {
-      s_off = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
-    } else {
-      const int64_t blk0 = t.n0 / 128;
-      const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
-      const int64_t bsel = lane < 1 ? 0 : blk1;
-      s_off = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
-    }
-  };
-  auto row_off = [&](int i, uint32_t last, uint32_t ld) {
-    return min((uint32_t)(i * C::kRowsPerRound) + lrow, last) * ld + g16;
-  };
-
-  // ---- global -> LDS cursor: runs two steps ahead of the MFMAs -------------
-  // Step s is chunk s % nc of the workgroup's (s / nc)-th tile and lives in
-  // stage s % 2. The cursor (dtk, dc) is the next step to load; d_ak, d_bk,
-  // d_sk point at its chunk of A, B and the wave's scale vector. A step goes
-  // out as kParts load instructions per wave, issued one per MFMA by part(q)
-  // so that no wave stalls on a burst of loads. After the last step the
-  // cursor stays put: the remaining loads repeat that step into a stage no
-  // one reads any more (the kernel waits for them before it ends), which
-  // keeps every load unconditional.
-  constexpr int kParts = 2 * C::kRounds + 1;
-  int dtk = 0, dc = 0;
-  const uint8_t* d_ak;
-  const uint8_t* d_bk;
-  const float* d_sk;
-  // per-step advance of the wave's scale pointer: activation scales are
-  // chunk-major; FPROP block scales are contiguous along K, DGRAD's and the
-  // WGRAD column scales chunk-major
-  const int64_t s_step = wave < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
-  auto cursor_tile = [&]() {
-    const Tile t = make_tile<GROUPED>(p, g, start + local + nper * dtk);
-    set_offsets(t);
-    d_ak = p.a + t.m0 * p.lda;
-    d_bk = t.b + t.n0 * p.ldb;
-    if (wave < 4) d_sk = p.sa + t.m0;
-    else if constexpr (KIND == KIND_WGRAD) d_sk = t.sb + t.n0;
-    else if constexpr (KIND == KIND_FPROP) d_sk = t.sb + (t.n0 / 128) * p.ldsb;
-    else d_sk = t.sb + t.n0 / 128;
-  };
-  auto advance = [&]() {
-    if (dc + 1 < nc) {
-      ++dc;
-      d_ak += BK;
-      d_bk += BK;
-      d_sk += s_step;
-    } else if (dtk + 1 < my_tiles) {
-      dc = 0;
-      ++dtk;
-      cursor_tile();
-    }
-  };
-  cursor_tile();
-  auto part = [&](int q, int st) {
-    const uint32_t base = lds_addr(smem) + (uint32_t)(st * kStage);
-    if (q < 2 * C::kRounds) {
-      if (wave >= C::kLoaders) return;
-      if (q < C::kRounds)
-        dma16(d_ak, row_off(q, a_last, (uint32_t)p.lda), base + (q * C::kRowsPerRound + 8 * wave) * BK);
-      else
-        dma16(d_bk, row_off(q - C::kRounds, b_last, (uint32_t)p.ldb),
-              base + kABytes + ((q - C::kRounds) * C::kRowsPerRound + 8 * wave) * BK);
-    } else if (wave < 4 || KIND == KIND_WGRAD) {
-      dma4(uniform_ptr(d_sk), s_off, base + (wave < 4 ? kSaOff : kSbOff) + 256 * (wave & 3));
-    } else if (wave == 4) {
-      // FPROP / DGRAD: the tile's two weight block scales; a load's cost
-      // follows its active lanes, so only two lanes take part
-      if (lane < 2) dma4(uniform_ptr(d_sk), s_off, base + kSbOff);
-    }
-  };
+  const Walk wk = make_walk(p);
+  if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
+  const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
+  Loader<KIND, GROUPED, C::kWaves, LOADERS> ld(p, g, wk, lds_addr(smem), wave, lane);
+  constexpr int kParts = decltype(ld)::kParts;
 
   // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
   // first row is a multiple of 16: row r = base + l16, logical slots 2 lq, 2 lq + 1.
@@ -338,13 +381,13 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
   };
 
 #pragma unroll
-  for (int q = 0; q < kParts; ++q) part(q, 0);
-  advance();
+  for (int q = 0; q < kParts; ++q) ld.part(q, 0);
+  ld.advance();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < kParts; ++q) part(q, 1);
-  advance();
+  for (int q = 0; q < kParts; ++q) ld.part(q, 1);
+  ld.advance();
 
   // Weight fragments are read kBAhead columns before their MFMAs (one column
   // for WGRAD, whose column scales take the registers). bw[0] is the current
@@ -434,9 +477,9 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
             if (t >= kFirst) {
 #pragma unroll
               for (int q = 0; q < kParts; ++q)
-                if (q * kSlots / kParts == t - kFirst) part(q, s & 1);
+                if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
             }
-            if (t + 1 == kNT) advance();
+            if (t + 1 == kNT) ld.advance();
           }
           // keep this order: one MFMA, the fold of the result kLag MFMAs old,
           // then the reads due here (no result waits for the matrix core, and
@@ -457,7 +500,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
       fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], sbj[(u / C::TM) & 1]);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
-    const Tile cur = make_tile<GROUPED>(p, g, start + local + nper * tk);
+    const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       const int64_t row = cur.m0 + wave_m * C::WM + i * 16 + l16;
@@ -489,6 +532,171 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, LOADERS>::kThreads)) void ge
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Power-of-two scales applied by the matrix unit.
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0 exponent byte per lane for
+// each operand: lane l scales row l % 16 of its operand over K-block l / 16
+// (probed on gfx950). With power-of-two scales s = 2^k the byte is the fp32
+// exponent field (k + 127; 0 for the subnormal 2^-127) and every K-block of a
+// row carries its tile's scale, so the instruction itself multiplies each
+// product by s_a * s_b — the "MMA with group scaling" the report asks hardware
+// for (section 3.5.2) — and adds the scaled chunk sum into the FP32 accumulator
+// (C = acc), which it does block by block (8 products at a time) rather than
+// with one rounding. No VALU promotion is left, so the accumulator can live in
+// the AGPRs: 128 x 128 wave tiles (256 accumulators), 4 waves (one per SIMD),
+// workgroup tile 256 x 256, the same stages, loads and tile walk as above.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+
+template <int KIND, bool GROUPED>
+__global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g) {
+  constexpr int WAVES_M = 2, WM = 128, WN = 128, TM = WM / 16, TN = WN / 16, kNT = TM * TN;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WAVES_M;
+  const int wave_n = wave / WAVES_M;
+  const int l16 = lane & 15, lq = lane >> 4;
+
+  const Walk wk = make_walk(p);
+  if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
+  const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
+  Loader<KIND, GROUPED, 4, 4> ld(p, g, wk, lds_addr(smem), wave, lane);
+  constexpr int kParts = decltype(ld)::kParts;
+
+  const int sw = swz(l16);
+  const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
+  const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
+  auto a_frag = [&](const uint8_t* stage, int i) { return frag(stage + (wave_m * WM + i * 16) * BK, off0, off1); };
+  auto b_frag = [&](const uint8_t* stage, int j) {
+    return frag(stage + kABytes + (wave_n * WN + j * 16) * BK, off0, off1);
+  };
+  // Exponent bytes of one step: ea[i] of this lane's activation row in subtile
+  // i; eb[j] of its weight row in subtile j (one block scale per wave except
+  // for WGRAD's row scales).
+  auto read_exps = [&](const uint8_t* stage, int (&ea)[TM], int (&eb)[TN]) {
+    const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
+    const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ea[i] = e8m0(Sa[wave_m * WM + i * 16 + l16]);
+    if constexpr (KIND == KIND_WGRAD) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) eb[j] = e8m0(Sb[wave_n * WN + j * 16 + l16]);
+    } else {
+      const int e = e8m0(Sb[wave_n]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) eb[j] = e;
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < kParts; ++q) ld.part(q, 0);
+  ld.advance();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kParts; ++q) ld.part(q, 1);
+  ld.advance();
+
+  // Weight fragments are read kBAhead columns before their MFMAs; the barrier
+  // precedes column kBarCol, the first whose look-ahead read falls into the
+  // next step's stage. Activation fragments of the next step are read right
+  // after their last use in the current one.
+  constexpr int kBAhead = 2;
+  constexpr int kBarCol = TN - kBAhead;
+  v8i bw[kBAhead + 1];
+#pragma unroll
+  for (int q = 0; q < kBAhead; ++q) bw[q] = b_frag(smem, q);
+  v8i af[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) af[i] = a_frag(smem, i);
+  int ea[TM], eb[TN], ean[TM], ebn[TN];
+  read_exps(smem, ea, eb);
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  int s = 0;
+#pragma clang loop unroll(disable)
+  for (int tk = 0; tk < my_tiles; ++tk) {
+#pragma clang loop unroll(disable)
+    for (int c = 0; c < nc; ++c, ++s) {
+      const uint8_t* stage = smem + (s & 1) * kStage;
+      const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if (j == kBarCol) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          read_exps(nstage, ean, ebn);
+        }
+        bw[kBAhead] = j + kBAhead < TN ? b_frag(stage, j + kBAhead) : b_frag(nstage, j + kBAhead - TN);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int t = j * TM + i;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], acc[i][j], 0, 0, 0, eb[j], 0,
+                                                                      ea[i]);
+          if (j + 1 == TN) af[i] = a_frag(nstage, i);
+          // the cursor's step into stage s % 2 (free since the barrier), its
+          // loads spread evenly over the MFMAs after the barrier
+          {
+            constexpr int kFirst = TM * kBarCol;
+            constexpr int kSlots = kNT - kFirst;
+            if (t >= kFirst) {
+#pragma unroll
+              for (int q = 0; q < kParts; ++q)
+                if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
+            }
+            if (t + 1 == kNT) ld.advance();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kBAhead; ++q) bw[q] = bw[q + 1];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ea[i] = ean[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) eb[j] = ebn[j];
+    }
+
+    // ---- tile done: epilogue --------------------------------------------------
+    const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t row = cur.m0 + wave_m * WM + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = cur.n0 + wave_n * WN + j * 16 + 4 * lq;
+        if (row < cur.m_end && col < cur.n_end) {
+          if constexpr (KIND == KIND_WGRAD) {
+            float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
+            *reinterpret_cast<v4f*>(o) = acc[i][j];
+          } else {
+            const bf16x2 lo = __builtin_convertvector((f32x2){acc[i][j][0], acc[i][j][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2){acc[i][j][2], acc[i][j][3]}, bf16x2);
+            uint2 packed;
+            __builtin_memcpy(&packed.x, &lo, 4);
+            __builtin_memcpy(&packed.y, &hi, 4);
+            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
+            *reinterpret_cast<uint2*>(o) = packed;
+          }
+        }
+        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  // the repeated loads after the last step must land before the workgroup's
+  // LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  (void)total;
+}
+
 GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda, const float* sa,
                    int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
                    void* out, int64_t ldo) {
@@ -508,7 +716,7 @@ constexpr int kWN = 2;   // 256 VGPRs the VALU can address, with room for fragme
 #define FP8BQ_LOADERS 8
 #endif
 constexpr int kLd = FP8BQ_LOADERS;   // waves issuing the operand loads
-constexpr int kBlock = Cfg<kWM, kWN, kLd>::kThreads;
+constexpr int kBlock = Cfg<kWM, kWN>::kThreads;
 
 // One workgroup per CU (the LDS stages take most of a CU's 160 KB): as many
 // workgroups as CUs, or as tiles when there are fewer tiles.
@@ -526,11 +734,20 @@ int persistent_grid(int tiles) {
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
                        const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
-                       const float* sb, int64_t ldsb, void* out, int64_t ldo, hipStream_t st) {
+                       const float* sb, int64_t ldsb, void* out, int64_t ldo, bool pow2, hipStream_t st) {
   GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   GroupArgs g;
   g.groups = 0;
   const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
+  if (pow2) {
+    const dim3 block4(256);
+    switch (kind) {
+      case KIND_FPROP: hipLaunchKernelGGL((gemm_pow2_kernel<KIND_FPROP, false>), grid, block4, 0, st, p, g); break;
+      case KIND_DGRAD: hipLaunchKernelGGL((gemm_pow2_kernel<KIND_DGRAD, false>), grid, block4, 0, st, p, g); break;
+      default:         hipLaunchKernelGGL((gemm_pow2_kernel<KIND_WGRAD, false>), grid, block4, 0, st, p, g); break;
+    }
+    return hipGetLastError();
+  }
   switch (kind) {
     case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
     case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
@@ -542,7 +759,7 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
 hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, int64_t k,
                                const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                                const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                               uint16_t* out, int64_t ldo, hipStream_t st) {
+                               uint16_t* out, int64_t ldo, bool pow2, hipStream_t st) {
   GroupArgs g;
   g.groups = groups;
   int tiles = 0;
@@ -557,7 +774,10 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, in
   p.tiles_m = tiles;
   if (tiles == 0) return hipSuccess;   // every group empty: nothing to compute
   const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
-  hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN, kLd>), grid, block, 0, st, p, g);
+  if (pow2)
+    hipLaunchKernelGGL((gemm_pow2_kernel<KIND_FPROP, true>), grid, dim3(256), 0, st, p, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN, kLd>), grid, block, 0, st, p, g);
   return hipGetLastError();
 }
 

@@ -9,19 +9,20 @@ namespace fp8bq {
 
 // Launchers. Arguments have been validated by the entry points; each returns
 // the hipError_t of its launch.
+// pow2: power-of-two scales (otherwise s = absmax / 448).
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st);
 hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* qt, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                                 uint8_t* qt, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st);
 hipError_t launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, uint8_t* q,
                           int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
-                          hipStream_t st);
+                          bool pow2, hipStream_t st);
 
 enum GemmKind { KIND_FPROP = 0, KIND_DGRAD = 1, KIND_WGRAD = 2 };
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
                        const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
-                       const float* sb, int64_t ldsb, void* out, int64_t ldo, hipStream_t st);
+                       const float* sb, int64_t ldsb, void* out, int64_t ldo, bool pow2, hipStream_t st);
 
 // Largest group count the grouped GEMM accepts (offsets travel as kernel arguments).
 constexpr int kMaxGroups = 256;
@@ -29,6 +30,6 @@ constexpr int kMaxGroups = 256;
 hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, int64_t k,
                                const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                                const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                               uint16_t* out, int64_t ldo, hipStream_t st);
+                               uint16_t* out, int64_t ldo, bool pow2, hipStream_t st);
 
 }  // namespace fp8bq

@@ -110,9 +110,36 @@ __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits16) {
   return t;
 }
 
-// Encodes four values (one output dword); `exact` codes are computed only when
-// the brackets disagree.
+// Power-of-two scale (the report's integral-power-of-2 scaling factors,
+// section 3.3.3): s = 2^k with k the smallest integer such that
+// amax <= 448 * 2^k, within [-127, 127] (an E8M0 exponent byte); an all-zero
+// group gets 2^-127. With 448 * 2^k = 1.75 * 2^(k+8), a normal bf16
+// amax = (1 + m/128) 2^(e-127) needs k = e - 135 when m <= 96 (mantissa
+// <= 1.75) and k = e - 134 otherwise; subnormal and tiny amax clamp to -127.
+// x * 2^-k is then exact (|x * 2^-k| <= 448; products that fall below the
+// fp32 normal range encode to zero either way), so one conversion rounds it.
+__device__ __forceinline__ TileScale make_scale_pow2(uint32_t amax_bits16) {
+  const int e = (int)((amax_bits16 >> 7) & 0xFF), m = (int)(amax_bits16 & 0x7F);
+  const int k = max(-127, min(127, e - 135 + (m > 96 ? 1 : 0)));
+  TileScale t;
+  t.s = k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(0x00400000u);
+  t.rlo = t.rhi = __uint_as_float((uint32_t)(127 - k) << 23);      // 2^-k, a normal fp32 for k <= 120
+  t.fast = true;
+  return t;
+}
+
+template <bool POW2>
+__device__ __forceinline__ TileScale group_scale(uint32_t amax_bits16) {
+  if constexpr (POW2) return make_scale_pow2(amax_bits16);
+  else return make_scale(amax_bits16);
+}
+
+// Encodes four values (one output dword). Exact scales: the exact codes are
+// computed only when the brackets disagree. Power-of-two scales: one exact
+// product and one conversion.
+template <bool POW2>
 __device__ __forceinline__ uint32_t encode4(float f0, float f1, float f2, float f3, const TileScale& t) {
+  if constexpr (POW2) return cvt4(f0 * t.rlo, f1 * t.rlo, f2 * t.rlo, f3 * t.rlo);
   const uint32_t lo = cvt4(f0 * t.rlo, f1 * t.rlo, f2 * t.rlo, f3 * t.rlo);
   const uint32_t hi = cvt4(f0 * t.rhi, f1 * t.rhi, f2 * t.rhi, f3 * t.rhi);
   if (__builtin_expect(t.fast && lo == hi, 1)) return lo;
@@ -120,10 +147,11 @@ __device__ __forceinline__ uint32_t encode4(float f0, float f1, float f2, float 
 }
 
 // Eight bf16 (packed in four dwords) -> eight codes.
+template <bool POW2>
 __device__ __forceinline__ uint2 encode8(const uint4 w, const TileScale& t) {
   uint2 r;
-  r.x = encode4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), t);
-  r.y = encode4(bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w), t);
+  r.x = encode4<POW2>(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), t);
+  r.y = encode4<POW2>(bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w), t);
   return r;
 }
 
@@ -138,6 +166,7 @@ __device__ __forceinline__ uint2 encode8(const uint4 w, const TileScale& t) {
 constexpr int kRowThreads = 256;
 constexpr int kRowsPerBlock = (kRowThreads / 64) * 8;
 
+template <bool POW2>
 __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int rows, uint8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
@@ -149,8 +178,8 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
   const uint16_t* p = x + (int64_t)row * ldx + col * 128 + l8 * 16;
   const uint4 v0 = *reinterpret_cast<const uint4*>(p);
   const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
-  const TileScale ts = make_scale(lane8_max(mag_max16(v0, v1)));
-  const uint2 a = encode8(v0, ts), b = encode8(v1, ts);
+  const TileScale ts = group_scale<POW2>(lane8_max(mag_max16(v0, v1)));
+  const uint2 a = encode8<POW2>(v0, ts), b = encode8<POW2>(v1, ts);
   if (r < rows) {
     *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + col * 128 + l8 * 16) = make_uint4(a.x, a.y, b.x, b.y);
     if (l8 == 0) s[(int64_t)col * lds + row] = ts.s;
@@ -168,6 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 constexpr int kColBlockCols = 64;
 constexpr int kColLdsStride = kColBlockCols / 2 + 1;   // dwords per staged row (+1 pad)
 
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
@@ -197,17 +227,17 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   }
   mlo = lane8_max(mlo);
   mhi = lane8_max(mhi);
-  const TileScale slo = make_scale(mlo), shi = make_scale(mhi);
+  const TileScale slo = group_scale<POW2>(mlo), shi = group_scale<POW2>(mhi);
 
   uint4 clo, chi;
-  clo.x = encode4(bf_lo(w[0]), bf_lo(w[1]), bf_lo(w[2]), bf_lo(w[3]), slo);
-  clo.y = encode4(bf_lo(w[4]), bf_lo(w[5]), bf_lo(w[6]), bf_lo(w[7]), slo);
-  clo.z = encode4(bf_lo(w[8]), bf_lo(w[9]), bf_lo(w[10]), bf_lo(w[11]), slo);
-  clo.w = encode4(bf_lo(w[12]), bf_lo(w[13]), bf_lo(w[14]), bf_lo(w[15]), slo);
-  chi.x = encode4(bf_hi(w[0]), bf_hi(w[1]), bf_hi(w[2]), bf_hi(w[3]), shi);
-  chi.y = encode4(bf_hi(w[4]), bf_hi(w[5]), bf_hi(w[6]), bf_hi(w[7]), shi);
-  chi.z = encode4(bf_hi(w[8]), bf_hi(w[9]), bf_hi(w[10]), bf_hi(w[11]), shi);
-  chi.w = encode4(bf_hi(w[12]), bf_hi(w[13]), bf_hi(w[14]), bf_hi(w[15]), shi);
+  clo.x = encode4<POW2>(bf_lo(w[0]), bf_lo(w[1]), bf_lo(w[2]), bf_lo(w[3]), slo);
+  clo.y = encode4<POW2>(bf_lo(w[4]), bf_lo(w[5]), bf_lo(w[6]), bf_lo(w[7]), slo);
+  clo.z = encode4<POW2>(bf_lo(w[8]), bf_lo(w[9]), bf_lo(w[10]), bf_lo(w[11]), slo);
+  clo.w = encode4<POW2>(bf_lo(w[12]), bf_lo(w[13]), bf_lo(w[14]), bf_lo(w[15]), slo);
+  chi.x = encode4<POW2>(bf_hi(w[0]), bf_hi(w[1]), bf_hi(w[2]), bf_hi(w[3]), shi);
+  chi.y = encode4<POW2>(bf_hi(w[4]), bf_hi(w[5]), bf_hi(w[6]), bf_hi(w[7]), shi);
+  chi.z = encode4<POW2>(bf_hi(w[8]), bf_hi(w[9]), bf_hi(w[10]), bf_hi(w[11]), shi);
+  chi.w = encode4<POW2>(bf_hi(w[12]), bf_hi(w[13]), bf_hi(w[14]), bf_hi(w[15]), shi);
 
   const int64_t col = c0 + 2 * p;
   *reinterpret_cast<uint4*>(qt + col * ldq + r0 + seg * 16) = clo;
@@ -231,6 +261,7 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_w_kernel(
     const uint16_t* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ s, int64_t lds, uint8_t* __restrict__ qt, int64_t ldqt) {
@@ -253,12 +284,12 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
   m = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
-  const TileScale ts = make_scale(m);
+  const TileScale ts = group_scale<POW2>(m);
   if (t == 0) s[(int64_t)blockIdx.y * lds + blockIdx.x] = ts.s;
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint2 c = encode8(v[i], ts);
+    const uint2 c = encode8<POW2>(v[i], ts);
     *reinterpret_cast<uint2*>(q + (n0 + r + 16 * i) * ldq + k0 + c8) = c;
     if (qt) {
       uint32_t* dst = codes + ((r + 16 * i) * kWStride + c8) / 4;
@@ -293,24 +324,33 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
 }  // namespace
 
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)(cols / 128));
-  hipLaunchKernelGGL(quant_act_rows_kernel, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, q, ldq, s, lds);
+  if (pow2)
+    hipLaunchKernelGGL(quant_act_rows_kernel<true>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, q, ldq, s, lds);
+  else
+    hipLaunchKernelGGL(quant_act_rows_kernel<false>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, q, ldq, s, lds);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                                 uint8_t* qt, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+                                 uint8_t* qt, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st) {
   dim3 grid((unsigned)(cols / kColBlockCols), (unsigned)(rows / 128));
-  hipLaunchKernelGGL(quant_act_cols_kernel, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
+  if (pow2)
+    hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
+  else
+    hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, uint8_t* q,
                           int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
-                          hipStream_t st) {
+                          bool pow2, hipStream_t st) {
   dim3 grid((unsigned)(k / 128), (unsigned)(n / 128));
-  hipLaunchKernelGGL(quant_w_kernel, grid, dim3(256), 0, st, w, ldw, q, ldq, s, lds, qt, ldqt);
+  if (pow2)
+    hipLaunchKernelGGL(quant_w_kernel<true>, grid, dim3(256), 0, st, w, ldw, q, ldq, s, lds, qt, ldqt);
+  else
+    hipLaunchKernelGGL(quant_w_kernel<false>, grid, dim3(256), 0, st, w, ldw, q, ldq, s, lds, qt, ldqt);
   return hipGetLastError();
 }
 

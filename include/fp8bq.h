@@ -28,6 +28,11 @@
  *   s = fl32(absmax / 448) (IEEE binary32 quotient, round-to-nearest-even);
  *   q = E4M3 round-to-nearest-even of fl32(x / s), saturating to +-448, sign
  *   kept for zeros; a tile whose absmax is 0 gets s = 0 and codes +0 / -0.
+ *   With FP8BQ_SCALE_POW2 (section 3.3.3 "low-precision storage and
+ *   communication": scaling factors that are integral powers of 2) the scale
+ *   is instead s = 2^k, k the smallest integer with absmax <= 448 * 2^k,
+ *   clamped to [-127, 127] (an E8M0 exponent byte); an all-zero tile gets
+ *   s = 2^-127; q = E4M3 round-to-nearest-even of the exact x * 2^-k.
  *   Inputs must be finite (NaN / Inf give unspecified codes and outputs).
  *
  * Conventions:
@@ -71,6 +76,11 @@ typedef enum {
 
 enum { FP8BQ_ACT_ROWWISE = 0, FP8BQ_ACT_COLWISE = 1 };
 
+/* Flag: power-of-two scales. OR-ed into the mode of fp8bq_quant_act_1x128,
+   passed as `flags` to fp8bq_quant_w_128x128, OR-ed into the op of
+   fp8bq_gemm (which then applies the scales inside the matrix instruction). */
+enum { FP8BQ_SCALE_POW2 = 0x10 };
+
 /*
  * Online activation quantisation (report section 3.3.2, Figure 7a; for the
  * column-wise mode section 3.3.3 "low-precision activations" and 3.5.2).
@@ -86,6 +96,7 @@ enum { FP8BQ_ACT_ROWWISE = 0, FP8BQ_ACT_COLWISE = 1 };
  *          q  E4M3 [cols, rows], ldq >= rows; q[j * ldq + r] encodes x[r][j].
  *          s  tile (rows [128c, 128c+128), column j) at s[c * lds + j],
  *             lds >= cols.
+ *        Either mode may be OR-ed with FP8BQ_SCALE_POW2 (power-of-two scales).
  * Errors: E_INVAL (null, rows/cols <= 0, ld too small, bad mode), E_SHAPE,
  *         E_ALIGN, E_DEVICE, E_HIP.
  */
@@ -102,11 +113,12 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
  * qt     optional (may be NULL): the transposed FP8 copy [k, n], ldqt >= n,
  *        qt[j * ldqt + i] == q[i * ldq + j]. It is the B operand of the Dgrad
  *        GEMM (block quantisation commutes with transposition).
- * Errors: as above.
+ * flags  0 (s = absmax / 448) or FP8BQ_SCALE_POW2 (power-of-two scales).
+ * Errors: as above; E_INVAL for unknown flags.
  */
 int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
                           void* q, int64_t ldq, float* s, int64_t lds,
-                          void* qt, int64_t ldqt, void* stream);
+                          void* qt, int64_t ldqt, int flags, void* stream);
 
 /*
  * Block-scaled FP8 GEMM with per-128-K-chunk promotion (report section 3.3.2
@@ -129,6 +141,14 @@ int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
  *                  ldsb >= n (column-wise activation quantisation output).
  * out    FPROP / DGRAD: bf16 [m, n] (round-to-nearest-even), ldo >= n.
  *        WGRAD: float [m, n], ldo >= n.
+ * op | FP8BQ_SCALE_POW2: every scale of sa and sb is a power of two in
+ *        [2^-127, 2^127], as the quantisers write with FP8BQ_SCALE_POW2 (only
+ *        the exponent field is read; other scales give wrong results). The
+ *        scales are applied inside the matrix instruction (E8M0 block scales)
+ *        and each chunk's scaled sum is accumulated in FP32 by the matrix unit
+ *        itself, which adds it in blocks of 8 products rather than in one
+ *        rounding (report section 3.3.2 asks hardware for exactly this
+ *        "MMA with group scaling"; error measured against the oracle).
  * Errors: as above.
  */
 int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k,
@@ -140,7 +160,7 @@ int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k,
  * Grouped (per-expert) Fprop for the MoE up-projection (report section 3.3.3
  * "low-precision communication": FP8 Fprop of the dispatched activations).
  *
- * groups   G >= 1 experts, G <= 1024.
+ * groups   G >= 1 experts, G <= 256.
  * row_off  HOST array of G + 1 int64: expert e owns rows [row_off[e],
  *          row_off[e+1]) of a and out; row_off[0] == 0, non-decreasing, every
  *          entry a multiple of 128 (pad each expert's rows, e.g. with zeros).
@@ -150,12 +170,14 @@ int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k,
  * sb       G block grids [n/128][k/128], row stride ldsb, expert e's at
  *          sb + e*(n/128)*ldsb.
  * out      bf16 [m, n], ldo >= n.
- * Errors: as above; E_SHAPE for bad offsets.
+ * flags    0, or FP8BQ_SCALE_POW2 for power-of-two scales applied by the matrix
+ *          instruction (as fp8bq_gemm with op | FP8BQ_SCALE_POW2).
+ * Errors: as above; E_SHAPE for bad offsets, E_INVAL for unknown flags.
  */
 int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
                        const void* a, int64_t lda, const float* sa, int64_t ldsa,
                        const void* b, int64_t ldb, const float* sb, int64_t ldsb,
-                       void* out, int64_t ldo, void* stream);
+                       void* out, int64_t ldo, int flags, void* stream);
 
 /* Thread-local description of the last non-OK status on this thread. */
 const char* fp8bq_last_error(void);

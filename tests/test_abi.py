@@ -56,6 +56,7 @@ def test_quant_act_validation(L):
     assert _st(L, f, *[None] + ok[1:]) == fb.E_INVAL
     assert _st(L, f, *ok[:1] + [0] + ok[2:]) == fb.E_INVAL                      # rows
     assert _st(L, f, *ok[:4] + [2] + ok[5:]) == fb.E_INVAL                      # mode
+    assert _st(L, f, *ok[:4] + [0x12] + ok[5:]) == fb.E_INVAL                   # mode with the pow2 flag
     assert _st(L, f, *ok[:3] + [1000] + ok[4:]) == fb.E_INVAL                   # ldx < cols
     assert _st(L, f, *ok[:2] + [1000, 1000] + ok[4:6] + [1000] + ok[7:]) == fb.E_SHAPE
     assert _st(L, f, *ok[:8] + [255, None]) == fb.E_INVAL                       # lds < rows
@@ -71,13 +72,15 @@ def test_quant_act_validation(L):
 
 def test_quant_w_validation(L):
     f = "fp8bq_quant_w_128x128"
-    ok = [A16, 256, 384, 384, B16, 384, S4, 3, O16, 256, None]
+    ok = [A16, 256, 384, 384, B16, 384, S4, 3, O16, 256, 0, None]
     assert _st(L, f, *[A16, 0] + ok[2:]) == fb.E_INVAL
     assert _st(L, f, *ok[:1] + [200, 384, 384] + ok[4:]) == fb.E_SHAPE
     assert _st(L, f, *ok[:7] + [2] + ok[8:]) == fb.E_INVAL                      # lds < k/128
-    assert _st(L, f, *ok[:9] + [128, None]) == fb.E_INVAL                       # ldqt < n
-    assert _st(L, f, *ok[:8] + [O16 + 1, 256, None]) == fb.E_ALIGN
+    assert _st(L, f, *ok[:9] + [128, 0, None]) == fb.E_INVAL                    # ldqt < n
+    assert _st(L, f, *ok[:8] + [O16 + 1, 256, 0, None]) == fb.E_ALIGN
     assert _st(L, f, *ok[:4] + [B16 + 8] + ok[5:]) == fb.E_ALIGN
+    assert _st(L, f, *ok[:10] + [0x20, None]) == fb.E_INVAL                     # unknown flag
+    assert "flags" in L.fp8bq_last_error().decode()
 
 
 def _gemm_ok(op=0):
@@ -108,6 +111,8 @@ def test_gemm_validation(L):
         assert _st(L, f, *bad) == fb.E_ALIGN
         bad = list(ok); bad[13] = 383
         assert _st(L, f, *bad) == fb.E_INVAL                                   # ldo < n
+        bad = list(ok); bad[0] = op | 0x20
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # unknown flag
 
 
 def test_grouped_validation(L):
@@ -116,7 +121,7 @@ def test_grouped_validation(L):
 
     def off(*v):
         return (ctypes.c_int64 * len(v))(*v)
-    base = [None, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56, O16, 2048, None]
+    base = [None, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56, O16, 2048, 0, None]
     assert _st(L, f, 0, off(0), *base[1:]) == fb.E_INVAL
     assert _st(L, f, 257, off(*([0] * 258)), *base[1:]) == fb.E_INVAL
     assert _st(L, f, 2, None, *base[1:]) == fb.E_INVAL
@@ -127,6 +132,8 @@ def test_grouped_validation(L):
     assert _st(L, f, 2, off(0, 256, 512), *bad[1:]) == fb.E_INVAL             # ldsa < m
     bad = list(base); bad[10] = 55
     assert _st(L, f, 2, off(0, 256, 512), *bad[1:]) == fb.E_INVAL             # ldsb < k/128
+    bad = list(base); bad[13] = 1
+    assert _st(L, f, 2, off(0, 256, 512), *bad[1:]) == fb.E_INVAL             # unknown flag
     assert isinstance(P, type)
 
 
@@ -148,8 +155,16 @@ def _no_device():
 def test_valid_arguments_without_device_report_e_device(L):
     assert _st(L, "fp8bq_gemm", *_gemm_ok(0)) == fb.E_DEVICE
     assert _st(L, "fp8bq_quant_act_1x128", A16, 256, 1024, 1024, 0, B16, 1024, S4, 256, None) == fb.E_DEVICE
-    assert _st(L, "fp8bq_quant_w_128x128", A16, 256, 384, 384, B16, 384, S4, 3, None, 0, None) == fb.E_DEVICE
+    assert _st(L, "fp8bq_quant_w_128x128", A16, 256, 384, 384, B16, 384, S4, 3, None, 0, 0, None) == fb.E_DEVICE
     off = (ctypes.c_int64 * 3)(0, 256, 512)
     assert _st(L, "fp8bq_grouped_gemm", 2, off, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56,
-               O16, 2048, None) == fb.E_DEVICE
+               O16, 2048, 0, None) == fb.E_DEVICE
+    # the power-of-two flag is accepted everywhere
+    pow2 = fb.SCALE_POW2
+    assert _st(L, "fp8bq_gemm", *([_gemm_ok(0)[0] | pow2] + _gemm_ok(0)[1:])) == fb.E_DEVICE
+    assert _st(L, "fp8bq_gemm", *([_gemm_ok(2)[0] | pow2] + _gemm_ok(2)[1:])) == fb.E_DEVICE
+    assert _st(L, "fp8bq_quant_act_1x128", A16, 256, 1024, 1024, 1 | pow2, B16, 256, S4, 1024, None) == fb.E_DEVICE
+    assert _st(L, "fp8bq_quant_w_128x128", A16, 256, 384, 384, B16, 384, S4, 3, None, 0, pow2, None) == fb.E_DEVICE
+    assert _st(L, "fp8bq_grouped_gemm", 2, off, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56,
+               O16, 2048, pow2, None) == fb.E_DEVICE
     assert "device" in L.fp8bq_last_error().decode()
