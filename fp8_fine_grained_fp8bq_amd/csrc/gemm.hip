@@ -204,6 +204,41 @@ __device__ __forceinline__ Walk make_walk(const GemmArgs& p) {
   return wk;
 }
 
+// ---- epilogue ----------------------------------------------------------------
+// Stores a wave's TM x TN subtiles (lane: output row l16 of subtile i, columns
+// 4 lq .. 4 lq + 3 of subtile j) as bf16 (round to nearest even, hardware
+// v_cvt_pk_bf16_f32, equal to the integer rounding on every finite fp32) or
+// fp32. Full tiles take one row pointer per subtile row and constant column
+// offsets; edge tiles check every row and column.
+template <int KIND, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
+                                           int64_t row0, int64_t col0) {
+  auto put = [&](int64_t row, int64_t col, const v4f& v) {
+    if constexpr (KIND == KIND_WGRAD) {
+      *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + row * p.ldo + col) = v;
+    } else {
+      const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+      uint2 packed;
+      __builtin_memcpy(&packed.x, &lo, 4);
+      __builtin_memcpy(&packed.y, &hi, 4);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col) = packed;
+    }
+  };
+  if (cur.m_end - cur.m0 == BM && cur.n_end - cur.n0 == BN) {   // uniform
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if (row0 + i * 16 < cur.m_end && col0 + j * 16 < cur.n_end) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
+  }
+}
+
 // ---- global -> LDS loads ----------------------------------------------------
 // Loader wave w (w < LOADERS) fills, in round i, tile rows
 // i * kRowsPerRound + 8 w + ln / 8 (lane ln), 16 bytes at physical slot
@@ -311,7 +346,9 @@ struct Loader {
   __device__ __forceinline__ void part(int q, int st) const {
     const uint32_t base = smem_base + (uint32_t)(st * kStage);
     if (q < 2 * kRounds) {
-      if (wave >= LOADERS) return;
+      if constexpr (LOADERS < WAVES) {
+        if (wave >= LOADERS) return;
+      }
       if (q < kRounds)
         dma16(d_ak, row_off(q, a_last, (uint32_t)p.lda), base + (q * kRowsPerRound + 8 * wave) * BK);
       else
@@ -320,8 +357,10 @@ struct Loader {
       return;
     }
     const int v = q - 2 * kRounds, sw = wave + v * WAVES;
-    if (sw < 4 || KIND == KIND_WGRAD) {
-      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (sw < 4 ? kSaOff : kSbOff) + 256 * (sw & 3));
+    // with four waves, scale wave v of wave w is w (activations) or w + 4
+    const bool act = WAVES == 4 ? v == 0 : sw < 4;
+    if (act || KIND == KIND_WGRAD) {
+      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (act ? kSaOff : kSbOff) + 256 * (sw & 3));
     } else if (sw == 4) {
       // FPROP / DGRAD: the tile's two weight block scales; a load's cost
       // follows its active lanes, so only two lanes take part
@@ -501,31 +540,11 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
     const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
+    store_tile<KIND, C::TM, C::TN>(p, cur, acc, cur.m0 + wave_m * C::WM + l16, cur.n0 + wave_n * C::WN + 4 * lq);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int64_t row = cur.m0 + wave_m * C::WM + i * 16 + l16;
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int64_t col = cur.n0 + wave_n * C::WN + j * 16 + 4 * lq;
-        if (row < cur.m_end && col < cur.n_end) {
-          if constexpr (KIND == KIND_WGRAD) {
-            float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
-            *reinterpret_cast<v4f*>(o) = acc[i][j];
-          } else {
-            // v_cvt_pk_bf16_f32 rounds to nearest even (equal to the integer
-            // rounding on every finite fp32, checked exhaustively on gfx950)
-            const bf16x2 lo = __builtin_convertvector((f32x2){acc[i][j][0], acc[i][j][1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector((f32x2){acc[i][j][2], acc[i][j][3]}, bf16x2);
-            uint2 packed;
-            __builtin_memcpy(&packed.x, &lo, 4);
-            __builtin_memcpy(&packed.y, &hi, 4);
-            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
-            *reinterpret_cast<uint2*>(o) = packed;
-          }
-        }
-        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   // the repeated loads after the last step must land before the workgroup's
   // LDS is released
@@ -641,6 +660,9 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
           const int t = j * TM + i;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], acc[i][j], 0, 0, 0, eb[j], 0,
                                                                       ea[i]);
+          // pins the MFMA here: its result feeds only later MFMAs, and the
+          // compiler would otherwise sink whole columns below the barrier
+          asm volatile("" : "+a"(acc[i][j]));
           if (j + 1 == TN) af[i] = a_frag(nstage, i);
           // the cursor's step into stage s % 2 (free since the barrier), its
           // loads spread evenly over the MFMAs after the barrier
@@ -667,29 +689,11 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
 
     // ---- tile done: epilogue --------------------------------------------------
     const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
+    store_tile<KIND, TM, TN>(p, cur, acc, cur.m0 + wave_m * WM + l16, cur.n0 + wave_n * WN + 4 * lq);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t row = cur.m0 + wave_m * WM + i * 16 + l16;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = cur.n0 + wave_n * WN + j * 16 + 4 * lq;
-        if (row < cur.m_end && col < cur.n_end) {
-          if constexpr (KIND == KIND_WGRAD) {
-            float* o = reinterpret_cast<float*>(p.out) + row * p.ldo + col;
-            *reinterpret_cast<v4f*>(o) = acc[i][j];
-          } else {
-            const bf16x2 lo = __builtin_convertvector((f32x2){acc[i][j][0], acc[i][j][1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector((f32x2){acc[i][j][2], acc[i][j][3]}, bf16x2);
-            uint2 packed;
-            __builtin_memcpy(&packed.x, &lo, 4);
-            __builtin_memcpy(&packed.y, &hi, 4);
-            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col;
-            *reinterpret_cast<uint2*>(o) = packed;
-          }
-        }
-        acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   // the repeated loads after the last step must land before the workgroup's
   // LDS is released
