@@ -43,6 +43,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -101,6 +102,33 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
 __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
+}
+// The same 16-byte LDS DMA through a raw buffer resource (base, byte bound):
+// a lane whose offset (VGPR, no scalar offset, no thread-id addressing) is at
+// or past the bound reads nothing from memory and its bytes come back as
+// zeros.
+__device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+// Raw buffer resource over [base, end) (bound capped at 4 GiB - 1: offsets
+// stay below 2 GiB), all words uniform.
+__device__ __forceinline__ u32x4 make_rsrc(const uint8_t* base, const uint8_t* end) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t n = end > base ? (uint64_t)(end - base) : 0;
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);   // stride 0: raw
+  r.z = __builtin_amdgcn_readfirstlane(n > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)n);
+  r.w = 0x00020000u;
+  return r;
+}
+// Moves a resource's base on by d bytes (d below its bound).
+__device__ __forceinline__ void bump_rsrc(u32x4& r, uint32_t d) {
+  const uint64_t b = (((uint64_t)r.y << 32) | r.x) + d;
+  r.x = (uint32_t)b;
+  r.y = (uint32_t)(b >> 32);
+  r.z = r.z == 0xFFFFFFFFu ? r.z : r.z - d;
 }
 
 // A pointer every lane holds the same value of, moved to scalar registers
@@ -245,9 +273,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
 // ln % 8, i.e. logical slot (ln % 8) ^ swz(row); with an even number of
 // loaders swz(row) = (ln / 8) ^ (w & 1) in every round, so a lane's slot is
 // fixed and only its row moves. The lane's byte offset from the tile's first
-// row is computed per load; rows past the end of the operand repeat its last
-// row (their results are never stored). Offsets are 32-bit (the host checks
-// that 256 rows of either operand span less than 2 GiB).
+// row in each round is the same for every step and every tile, so it is
+// computed once; the operand tiles are read through raw buffer resources whose
+// base is the step's chunk of the tile's first row and whose bound is the end
+// of the operand, so rows past the end read as zeros (their results are never
+// stored). Offsets are 32-bit (the host checks that 256 rows of either operand
+// span less than 2 GiB).
 // Scales are brought by eight "scale waves" of 64 lanes (each real wave plays
 // 8 / WAVES of them): scale waves 0-3 bring 64 activation scales each; 4-7
 // bring 64 column scales each (WGRAD), or scale wave 4 brings the tile's two
@@ -255,8 +286,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
 // first again when the tile has only one).
 //
 // The cursor (dtk, dc) is the next step to load: step s is chunk s % nc of the
-// workgroup's (s / nc)-th tile and lives in stage s % 2; d_ak, d_bk, d_sk point
-// at its chunk of A, B and the scale vectors. A step goes out as kParts load
+// workgroup's (s / nc)-th tile and lives in stage s % 2; rs_a, rs_b and d_sk
+// address its chunk of A, B and the scale vectors. A step goes out as kParts load
 // instructions per wave, part(0 .. kParts-1), and then advance() moves the
 // cursor on. After the last step the cursor stays put: further loads repeat
 // that step into a stage no one reads any more (the kernels wait for them
@@ -276,12 +307,11 @@ struct Loader {
   const uint32_t smem_base;
   const int wave, lane;
   const uint32_t lrow, g16;
-  uint32_t a_last = 0, b_last = 0;
+  uint32_t voff_a[kRounds], voff_b[kRounds];
   uint32_t s_off[kScaleWaves];
   int64_t s_step[kScaleWaves];
   const float* d_sk[kScaleWaves];
-  const uint8_t* d_ak = nullptr;
-  const uint8_t* d_bk = nullptr;
+  u32x4 rs_a, rs_b;
   int dtk = 0, dc = 0;
 
   __device__ __forceinline__ Loader(const GemmArgs& p_, const GroupArgs& g_, const Walk& wk_, uint32_t smem_base_,
@@ -296,15 +326,18 @@ struct Loader {
       const int sw = wave + v * WAVES;
       s_step[v] = sw < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
     }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      voff_a[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.lda + g16;
+      voff_b[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.ldb + g16;
+    }
     cursor_tile();
   }
 
   __device__ __forceinline__ void cursor_tile() {
     const Tile t = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * dtk);
-    a_last = (uint32_t)(t.m_end - t.m0 - 1);
-    b_last = (uint32_t)(t.n_end - t.n0 - 1);
-    d_ak = p.a + t.m0 * p.lda;
-    d_bk = t.b + t.n0 * p.ldb;
+    rs_a = make_rsrc(p.a + t.m0 * p.lda, p.a + (p.m - 1) * p.lda + p.k);
+    rs_b = make_rsrc(t.b + t.n0 * p.ldb, t.b + (p.n - 1) * p.ldb + p.k);
 #pragma unroll
     for (int v = 0; v < kScaleWaves; ++v) {
       const int sw = wave + v * WAVES, q4 = sw & 3;
@@ -327,8 +360,8 @@ struct Loader {
   __device__ __forceinline__ void advance() {
     if (dc + 1 < wk.nc) {
       ++dc;
-      d_ak += BK;
-      d_bk += BK;
+      bump_rsrc(rs_a, BK);
+      bump_rsrc(rs_b, BK);
 #pragma unroll
       for (int v = 0; v < kScaleWaves; ++v) d_sk[v] += s_step[v];
     } else if (dtk + 1 < wk.my_tiles) {
@@ -336,10 +369,6 @@ struct Loader {
       ++dtk;
       cursor_tile();
     }
-  }
-
-  __device__ __forceinline__ uint32_t row_off(int i, uint32_t last, uint32_t ld) const {
-    return min((uint32_t)(i * kRowsPerRound) + lrow, last) * ld + g16;
   }
 
   // Load instruction q of the cursor's step into stage st.
@@ -350,10 +379,9 @@ struct Loader {
         if (wave >= LOADERS) return;
       }
       if (q < kRounds)
-        dma16(d_ak, row_off(q, a_last, (uint32_t)p.lda), base + (q * kRowsPerRound + 8 * wave) * BK);
+        dma16_buf(rs_a, voff_a[q], base + (q * kRowsPerRound + 8 * wave) * BK);
       else
-        dma16(d_bk, row_off(q - kRounds, b_last, (uint32_t)p.ldb),
-              base + kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
+        dma16_buf(rs_b, voff_b[q - kRounds], base + kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
       return;
     }
     const int v = q - 2 * kRounds, sw = wave + v * WAVES;
@@ -565,6 +593,65 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
 // the AGPRs: 128 x 128 wave tiles (256 accumulators), 4 waves (one per SIMD),
 // workgroup tile 256 x 256, the same stages, loads and tile walk as above.
 // ---------------------------------------------------------------------------
+// Position t of the row / column pass order over an n x n grid of MFMAs:
+// row 0, column 0 (what is left of it), row 1, column 1, ...; end_a / end_b
+// name the operand whose last use this is (-1 if none).
+struct PassCell { int i, j, end_a, end_b; };
+constexpr PassCell pass_cell(int t, int n) {
+  int pos = 0;
+  for (int k = 0; k < n; ++k) {
+    for (int j = k; j < n; ++j, ++pos)
+      if (pos == t) return {k, j, j == n - 1 ? k : -1, (j == n - 1 && k == n - 1) ? k : -1};
+    for (int i = k + 1; i < n; ++i, ++pos)
+      if (pos == t) return {i, k, -1, i == n - 1 ? k : -1};
+  }
+  return {-1, -1, -1, -1};
+}
+// Position of the last MFMA that uses activation (weight) fragment k.
+constexpr int death_a(int k, int n) {
+  for (int t = 0; t < n * n; ++t) if (pass_cell(t, n).end_a == k) return t;
+  return -1;
+}
+constexpr int death_b(int k, int n) {
+  for (int t = 0; t < n * n; ++t) if (pass_cell(t, n).end_b == k) return t;
+  return -1;
+}
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// LDS reads (two per fragment) that the pass order issues after the MFMAs at
+// positions lo < t < hi.
+constexpr int frag_reads_between(int lo, int hi, int n) {
+  int r = 0;
+  for (int t = lo + 1; t < hi; ++t) {
+    const PassCell c = pass_cell(t, n);
+    r += 2 * ((c.end_a >= 0) + (c.end_b >= 0));
+  }
+  return r;
+}
+template <class F, int... T>
+__device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, T...>) {
+  (f(std::integral_constant<int, T>{}), ...);
+}
+
+// The scaled MFMA as a statement with its accumulator tied (destination = C):
+// written through the builtin, the register allocator moves accumulators
+// between AGPRs around the loop when all 256 hold them, costing copies and
+// hazard waits. It also fixes the MFMA's place in the schedule. The compiler
+// no longer sees the instruction's hazards, so it carries them itself: two
+// wait states ahead of it cover a VALU write of any of its operands just
+// before (the scale exponents, the cleared accumulators); reading results
+// needs mfma_results_ready().
+__device__ __forceinline__ void mfma_scaled(v4f& acc, const v8i& a, const v8i& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// Wait states between the last MFMAs and any other read of their results (more
+// than the longest XDL write-to-read requirement); the scheduling barrier keeps
+// every later instruction below them.
+__device__ __forceinline__ void mfma_results_ready() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
 
 template <int KIND, bool GROUPED>
@@ -595,18 +682,21 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
   // Exponent bytes of one step: ea[i] of this lane's activation row in subtile
   // i; eb[j] of its weight row in subtile j (one block scale per wave except
   // for WGRAD's row scales).
-  auto read_exps = [&](const uint8_t* stage, int (&ea)[TM], int (&eb)[TN]) {
+  // Scales of one step: ra[i] of this lane's activation row in subtile i; rb[j]
+  // of its weight row in subtile j (one block scale per wave except for
+  // WGRAD's row scales). The MFMA takes their exponent bytes.
+  auto read_scales = [&](const uint8_t* stage, float (&ra)[TM], float (&rb)[TN]) {
     const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
     const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ea[i] = e8m0(Sa[wave_m * WM + i * 16 + l16]);
+    for (int i = 0; i < TM; ++i) ra[i] = Sa[wave_m * WM + i * 16 + l16];
     if constexpr (KIND == KIND_WGRAD) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) eb[j] = e8m0(Sb[wave_n * WN + j * 16 + l16]);
+      for (int j = 0; j < TN; ++j) rb[j] = Sb[wave_n * WN + j * 16 + l16];
     } else {
-      const int e = e8m0(Sb[wave_n]);
+      const float v = Sb[wave_n];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) eb[j] = e;
+      for (int j = 0; j < TN; ++j) rb[j] = v;
     }
   };
 
@@ -619,73 +709,94 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
   for (int q = 0; q < kParts; ++q) ld.part(q, 1);
   ld.advance();
 
-  // Weight fragments are read kBAhead columns before their MFMAs; the barrier
-  // precedes column kBarCol, the first whose look-ahead read falls into the
-  // next step's stage. Activation fragments of the next step are read right
-  // after their last use in the current one.
-  constexpr int kBAhead = 2;
-  constexpr int kBarCol = TN - kBAhead;
-  v8i bw[kBAhead + 1];
-#pragma unroll
-  for (int q = 0; q < kBAhead; ++q) bw[q] = b_frag(smem, q);
-  v8i af[TM];
+  // A step's fragments all sit in registers before it starts. Its 64 MFMAs
+  // run row 0, column 0, row 1, column 1, ... (each pass over what is left of
+  // that row or column), so activation fragment k is dead after the row-k
+  // pass and weight fragment k after the column-k pass; the next step's copy
+  // of each is read into the same registers right then, which spreads the
+  // step's 16 fragment reads over the step instead of bunching them at its
+  // end. The stage a step was read from is therefore free once the step
+  // begins; the one barrier per step (after the row-0 pass, before the first
+  // read of the next stage) makes it free for every wave and the previous
+  // step's loads visible, and the loads of step s + 2 into stage s % 2 spread
+  // over kSlots MFMAs after it, leaving them the rest of the step to land.
+#ifndef FP8BQ_P2_SLOTS
+#define FP8BQ_P2_SLOTS 40
+#endif
+  constexpr int kFirst = TN;   // the barrier follows the row-0 pass
+  constexpr int kSlots = FP8BQ_P2_SLOTS;
+  static_assert(TM == TN, "the row / column pass order assumes square wave tiles");
+  static_assert(kFirst + kSlots <= kNT, "loads must be issued within the step");
+  // The compiler tracks at most 15 outstanding LDS reads; with more in
+  // flight where a loop iteration begins it waits for all of them before the
+  // first MFMA, which would expose the latency of the step's last reads. An
+  // explicit wait late in each step (for reads issued at least kDrainLag
+  // MFMAs earlier) keeps the count it carries across the loop below that.
+  constexpr int kDrainAt = kNT - 5, kDrainLag = 8;
+  constexpr int kExpReady = kFirst + 12;   // scales are read right after the barrier
+  constexpr int kDrainCnt = frag_reads_between(kDrainAt - kDrainLag, kDrainAt, TM) +
+                            2 * (pass_cell(kDrainAt, TM).end_a >= 0);
+  static_assert(kDrainCnt + frag_reads_between(kDrainAt, kNT, TM) + 2 * (pass_cell(kDrainAt, TM).end_b >= 0) <= 14,
+                "reads in flight at the end of a step must stay countable");
+  v8i af[TM], bf[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) af[i] = a_frag(smem, i);
-  int ea[TM], eb[TN], ean[TM], ebn[TN];
-  read_exps(smem, ea, eb);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bf[j] = b_frag(smem, j);
+  int ea[TM], eb[TN];
+  float ran[TM], rbn[TN];
+  read_scales(smem, ran, rbn);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) ea[i] = e8m0(ran[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) eb[j] = e8m0(rbn[j]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the prologue's reads, for the same reason
 
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
   int s = 0;
+  auto step = [&]() {
+    const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
+    for_each_const([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr PassCell c = pass_cell(t, TM);
+      mfma_scaled(acc[c.i][c.j], bf[c.j], af[c.i], eb[c.j], ea[c.i]);
+      if constexpr (t >= kFirst && t < kFirst + kSlots) {
+#pragma unroll
+        for (int q = 0; q < kParts; ++q)
+          if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
+      }
+      if constexpr (t + 1 == kNT) ld.advance();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (c.end_a >= 0) {
+        if constexpr (c.end_a == 0) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          read_scales(nstage, ran, rbn);
+        }
+        af[c.end_a] = a_frag(nstage, c.end_a);
+      }
+      // the next step's exponent of row (column) k replaces this step's once
+      // both its last use has passed and the scale read has had time to land
+      for_each_const([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (cmax(death_a(k, TM), kExpReady) == t) ea[k] = e8m0(ran[k]);
+        if constexpr (cmax(death_b(k, TN), kExpReady) == t) eb[k] = e8m0(rbn[k]);
+      }, std::make_integer_sequence<int, TM>{});
+      if constexpr (t == kDrainAt) __builtin_amdgcn_s_waitcnt(0xC07F | (kDrainCnt << 8));
+      if constexpr (c.end_b >= 0) bf[c.end_b] = b_frag(nstage, c.end_b);
+    }, std::make_integer_sequence<int, kNT>{});
+    ++s;
+  };
+
 #pragma clang loop unroll(disable)
   for (int tk = 0; tk < my_tiles; ++tk) {
 #pragma clang loop unroll(disable)
-    for (int c = 0; c < nc; ++c, ++s) {
-      const uint8_t* stage = smem + (s & 1) * kStage;
-      const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if (j == kBarCol) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          read_exps(nstage, ean, ebn);
-        }
-        bw[kBAhead] = j + kBAhead < TN ? b_frag(stage, j + kBAhead) : b_frag(nstage, j + kBAhead - TN);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int t = j * TM + i;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], acc[i][j], 0, 0, 0, eb[j], 0,
-                                                                      ea[i]);
-          // pins the MFMA here: its result feeds only later MFMAs, and the
-          // compiler would otherwise sink whole columns below the barrier
-          asm volatile("" : "+a"(acc[i][j]));
-          if (j + 1 == TN) af[i] = a_frag(nstage, i);
-          // the cursor's step into stage s % 2 (free since the barrier), its
-          // loads spread evenly over the MFMAs after the barrier
-          {
-            constexpr int kFirst = TM * kBarCol;
-            constexpr int kSlots = kNT - kFirst;
-            if (t >= kFirst) {
-#pragma unroll
-              for (int q = 0; q < kParts; ++q)
-                if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
-            }
-            if (t + 1 == kNT) ld.advance();
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < kBAhead; ++q) bw[q] = bw[q + 1];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) ea[i] = ean[i];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) eb[j] = ebn[j];
-    }
+    for (int c = 0; c < nc; ++c) step();
+    mfma_results_ready();
 
     // ---- tile done: epilogue --------------------------------------------------
     const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
