@@ -199,6 +199,10 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g,
     t.m_end = min(t.m0 + BM, (int64_t)g.row_off128[e + 1] * 128);
     t.b += (int64_t)e * p.n * p.ldb;
     t.sb += (int64_t)e * (p.n / 128) * p.ldsb;
+    // the group table is read with scalar loads, which complete out of order
+    // with LDS reads: wait for them here, or every later LDS wait the compiler
+    // places would have to wait for everything
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   } else {
     t.m0 = (int64_t)tmi * BM;
     t.m_end = min(t.m0 + BM, p.m);
@@ -470,6 +474,11 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   for (int i = 0; i < C::TM; ++i) af[i] = a_frag(smem, i);
   float sc[C::TM], scp[C::TM], scn[C::TM];
   read_scales(smem, sc);
+  // The compiler tracks at most 15 outstanding LDS reads; with more in flight
+  // where a loop iteration begins it waits for all of them before the first
+  // MFMA. This wait and the one at the last column keep the count it carries
+  // into the loop below that.
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 
   v4f acc[C::TM][C::TN];
 #pragma unroll
@@ -512,6 +521,9 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
           __syncthreads();
           read_scales(nstage, scn);
         }
+        // last column: everything read before the previous column's weight
+        // fragment has landed (read at least a column ago)
+        if (j + 1 == C::TN) __builtin_amdgcn_s_waitcnt(0xC07F | (2 << 8));
         bw[kBAhead] = j + kBAhead < C::TN ? b_frag(stage, j + kBAhead) : b_frag(nstage, j + kBAhead - C::TN);
         // WGRAD column scales of column j (the last column's are read before
         // the barrier, below: after it the stage is being refilled)
@@ -758,7 +770,10 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   int s = 0;
-  auto step = [&]() {
+  // wait_loads: the step's barrier also waits for this wave's loads of the
+  // next stage; a tile's first step skips that, its epilogue waited for them
+  // before storing, so the stores stay in flight until the next step.
+  auto step = [&](bool wait_loads) {
     const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
     for_each_const([&](auto tc) {
       constexpr int t = decltype(tc)::value;
@@ -773,7 +788,7 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (c.end_a >= 0) {
         if constexpr (c.end_a == 0) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (wait_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
           read_scales(nstage, ran, rbn);
         }
@@ -795,8 +810,9 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
 #pragma clang loop unroll(disable)
   for (int tk = 0; tk < my_tiles; ++tk) {
 #pragma clang loop unroll(disable)
-    for (int c = 0; c < nc; ++c) step();
+    for (int c = 0; c < nc; ++c) step(c != 0 || tk == 0);
     mfma_results_ready();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the loads the next tile's first step reads
 
     // ---- tile done: epilogue --------------------------------------------------
     const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
