@@ -149,6 +149,24 @@ def main():
         quant_w()
         gemm()
 
+    # the same step with power-of-two scales (the matrix instruction applies them)
+    def quant_x_p2():
+        fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | fb.SCALE_POW2, xq.data_ptr(), K,
+                                 xs.data_ptr(), M, sp)
+
+    def quant_w_p2():
+        fb.fp8bq_quant_w_128x128(w.data_ptr(), N, K, K, wq.data_ptr(), K, ws.data_ptr(), K // 128, None, N,
+                                 fb.SCALE_POW2, sp)
+
+    def gemm_p2():
+        fb.fp8bq_gemm(fb.FPROP | fb.SCALE_POW2, M, N, K, xq.data_ptr(), K, xs.data_ptr(), M, wq.data_ptr(), K,
+                      ws.data_ptr(), K // 128, y.data_ptr(), N, sp)
+
+    def step_p2():
+        quant_x_p2()
+        quant_w_p2()
+        gemm_p2()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -181,6 +199,19 @@ def main():
             b.synchronize()
             durs.append(a.elapsed_time(b) * 1e3)
         return float(np.mean(durs)), float(np.median(durs))
+
+    # power-of-two variant: the same number of timed steps
+    for _ in range(args.warmup):
+        step_p2()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step_p2()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_p2 = ev0.elapsed_time(ev1) / args.steps
+    tg_p2, _ = time_kernel(gemm_p2, args.kernel_reps, False)
+    log(f"[bench] power-of-two scales: {ms_step_p2:.3f} ms/step, GEMM {tg_p2:.1f} us")
 
     tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
     tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
@@ -236,6 +267,15 @@ def main():
             "quant_w_frac_hbm": round(bytes_qw / tq_w / 1e3 / PEAK_HBM_GBS, 4),
             "gemm_us": round(tg, 2), "gemm_TFLOPs": round(gemm_tflops, 1),
             "quant_timing": "each kernel alone after a 512 MB read (MALL evicted), HIP events, mean",
+        },
+        "variants": {
+            "pow2_scales": {
+                "what": "the same step with power-of-two scales, applied by the scaled matrix instruction",
+                "value": round(flops / (ms_step_p2 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms_step_p2, 4), "gemm_us": round(tg_p2, 2),
+                "gemm_TFLOPs": round(flops / (tg_p2 * 1e-6) / 1e12, 1),
+                "kernel": "gemm_pow2_kernel<FPROP>",
+            },
         },
     }
     print(json.dumps(out), flush=True)
