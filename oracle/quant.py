@@ -152,6 +152,39 @@ def dequant_act(q: np.ndarray, s: np.ndarray) -> np.ndarray:
             * s.astype(np.float64)[..., None]).reshape(rows, cols)
 
 
+def requant_128x1(q: np.ndarray, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Transposing re-quantisation of an FP8 activation cache, 1x128 -> 128x1.
+
+    The report (section 3.5.2, "support for transposed GEMM") describes the
+    backward step: the forward pass stored activations as 1x128 FP8 tiles; the
+    weight-gradient GEMM needs them as 128x1 tiles, so they are read,
+    dequantised, transposed, re-quantised and stored again. For exactly these
+    activations the report (section 3.3.3, "low-precision storage and
+    communication") makes every scale an integral power of two, so that the
+    conversion adds no quantisation error of its own.
+
+    Steps: x_hat = dec(q) * s (float64, exact); 128x1 groups (128 consecutive
+    rows of one column); the group's scale is the power of two of
+    `pow2_exponent` on its exact absmax; codes E4M3(fl32(x_hat * 2^-k)). With
+    power-of-two input scales the product is exact in float32 too, and for
+    values that fit bf16 this is the 128x1 power-of-two quantisation of x_hat.
+
+    q uint8 [rows, cols] with s float32 [rows, cols // 128] (the natural layout
+    of `quant_act_1x128`). Returns qT uint8 [cols, rows] and sT float32
+    [cols, rows // 128], like `quant_act_128x1`.
+    """
+    rows, cols = q.shape
+    assert rows % TILE == 0 and cols % TILE == 0, "dimensions must be multiples of 128"
+    xh = dequant_act(q, s)                                         # exact
+    g = np.ascontiguousarray(xh.T).reshape(cols, rows // TILE, TILE)
+    amax = np.max(np.abs(g), axis=-1)
+    k = pow2_exponent(amax)
+    v = (g * np.ldexp(1.0, -k)[..., None]).astype(np.float32)      # exact product, one fp32 rounding
+    qt = e4m3.encode(v)
+    st = np.ldexp(np.float32(1.0), k.astype(np.int32)).astype(np.float32)
+    return qt.reshape(cols, rows), st
+
+
 def dequant_w(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """w_hat = dec(q) * s per 128x128 block, in float64 (exact)."""
     return e4m3.decode(q) * np.repeat(np.repeat(s.astype(np.float64), TILE, 0), TILE, 1)
