@@ -213,6 +213,20 @@ def main():
     tg_p2, _ = time_kernel(gemm_p2, args.kernel_reps, False)
     log(f"[bench] power-of-two scales: {ms_step_p2:.3f} ms/step, GEMM {tg_p2:.1f} us")
 
+    # transposing re-quantisation (1x128 -> 128x1) of the power-of-two cache of X
+    # that step_p2 left in xq / xs
+    xqt = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    xst = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+
+    def requant():
+        fb.fp8bq_requant_t_128x1(xq.data_ptr(), M, K, K, xs.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(), K,
+                                 0, sp)
+
+    requant()
+    t_rq, _ = time_kernel(requant, args.kernel_reps, True)
+    bytes_rq = 2 * M * K + 2 * (M * (K // 128) * 4)
+    log(f"[bench] requant 1x128 -> 128x1: {t_rq:.1f} us ({bytes_rq / t_rq / 1e3:.0f} GB/s)")
+
     tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
     tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
     tg, tg_med = time_kernel(gemm, args.kernel_reps, False)
@@ -266,6 +280,8 @@ def main():
             "quant_w_us": round(tq_w, 2), "quant_w_GBps": round(bytes_qw / tq_w / 1e3, 1),
             "quant_w_frac_hbm": round(bytes_qw / tq_w / 1e3 / PEAK_HBM_GBS, 4),
             "gemm_us": round(tg, 2), "gemm_TFLOPs": round(gemm_tflops, 1),
+            "requant_t_us": round(t_rq, 2), "requant_t_GBps": round(bytes_rq / t_rq / 1e3, 1),
+            "requant_t_frac_hbm": round(bytes_rq / t_rq / 1e3 / PEAK_HBM_GBS, 4),
             "quant_timing": "each kernel alone after a 512 MB read (MALL evicted), HIP events, mean",
         },
         "variants": {

@@ -31,8 +31,8 @@ FPROP, DGRAD, WGRAD = 0, 1, 2
 ACT_ROWWISE, ACT_COLWISE = 0, 1
 SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
-EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm",
-           "fp8bq_last_error", "fp8bq_version")
+EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
+           "fp8bq_grouped_gemm", "fp8bq_last_error", "fp8bq_version")
 
 
 class Fp8bqError(RuntimeError):
@@ -55,10 +55,12 @@ def lib() -> ctypes.CDLL:
         i64, vp, fp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
         L.fp8bq_quant_act_1x128.argtypes = [vp, i64, i64, i64, i32, vp, i64, fp, i64, vp]
         L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, i32, vp]
+        L.fp8bq_requant_t_128x1.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, fp, i64, i32, vp]
         L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
         L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
                                          vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, i32, vp]
-        for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm"):
+        for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
+                  "fp8bq_grouped_gemm"):
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
         L.fp8bq_last_error.argtypes = []
@@ -86,6 +88,11 @@ def fp8bq_quant_act_1x128(x, rows, cols, ldx, mode, q, ldq, s, lds, stream=0):
 def fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, flags=0, stream=0):
     return _check("fp8bq_quant_w_128x128",
                   lib().fp8bq_quant_w_128x128(w, n, k, ldw, q, ldq, s, lds, qt, ldqt, flags, stream))
+
+
+def fp8bq_requant_t_128x1(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, flags=0, stream=0):
+    return _check("fp8bq_requant_t_128x1",
+                  lib().fp8bq_requant_t_128x1(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, flags, stream))
 
 
 def fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
@@ -154,6 +161,23 @@ def quant_w_128x128(w, transposed_copy: bool = False, pow2: bool = False):
     fp8bq_quant_w_128x128(w.data_ptr(), n, k, w.stride(0), q.data_ptr(), k, s.data_ptr(), k // 128,
                           qt.data_ptr() if qt is not None else None, n, SCALE_POW2 if pow2 else 0, _stream(w))
     return q, s, qt
+
+
+def requant_t_128x1(q, s):
+    """FP8 activation cache q uint8 [rows, cols] with chunk-major 1x128 scales s [cols/128, >=rows]
+    -> (qt uint8 [cols, rows], st float32 [rows/128, cols]): 128x1 tiles with power-of-two scales,
+    the layout of COLWISE quantisation."""
+    import torch
+    if q.dtype != torch.uint8 or q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError("q must be a 2-D row-major uint8 tensor")
+    if s.dtype != torch.float32 or s.dim() != 2 or s.stride(1) != 1:
+        raise ValueError("s must be a 2-D row-major float32 tensor")
+    rows, cols = q.shape
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=q.device)
+    st = torch.empty((rows // 128, cols), dtype=torch.float32, device=q.device)
+    fp8bq_requant_t_128x1(q.data_ptr(), rows, cols, q.stride(0), s.data_ptr(), s.stride(0), qt.data_ptr(), rows,
+                          st.data_ptr(), cols, 0, _stream(q))
+    return qt, st
 
 
 def gemm(op: int, a, sa, b, sb, out=None):

@@ -99,6 +99,25 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
                                                static_cast<uint8_t*>(q), ldq, s, lds, pow2, str), "quant_act");
 }
 
+int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
+                          void* qt, int64_t ldqt, float* st, int64_t ldst, int flags, void* stream) {
+  if (!q || !s || !qt || !st) return fail(FP8BQ_E_INVAL, "requant_t: null pointer");
+  if (flags) return fail(FP8BQ_E_INVAL, "requant_t: flags must be 0, got %d", flags);
+  if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "requant_t: rows and cols must be positive");
+  if (ldq < cols || ldqt < rows) return fail(FP8BQ_E_INVAL, "requant_t: ldq must be >= cols and ldqt >= rows");
+  if (lds < rows || ldst < cols) return fail(FP8BQ_E_INVAL, "requant_t: lds must be >= rows and ldst >= cols");
+  if (rows % 128 || cols % 128)
+    return fail(FP8BQ_E_SHAPE, "requant_t: rows (%lld) and cols (%lld) must be multiples of 128", (long long)rows, (long long)cols);
+  if (rows / 128 > 65535 || cols / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "requant_t: too large");
+  if (!aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 4) || !aligned(st, 4))
+    return fail(FP8BQ_E_ALIGN, "requant_t: q and qt must be 16-byte aligned, scales 4-byte aligned");
+  if (ldq % 16 || ldqt % 16) return fail(FP8BQ_E_ALIGN, "requant_t: ldq and ldqt must be multiples of 16");
+  if (int stt = check_device()) return stt;
+  return launched(fp8bq::launch_requant_t(static_cast<const uint8_t*>(q), rows, cols, ldq, s, lds,
+                                          static_cast<uint8_t*>(qt), ldqt, st, ldst,
+                                          reinterpret_cast<hipStream_t>(stream)), "requant_t");
+}
+
 int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw, void* q, int64_t ldq,
                           float* s, int64_t lds, void* qt, int64_t ldqt, int flags, void* stream) {
   if (!w || !q || !s) return fail(FP8BQ_E_INVAL, "quant_w: null pointer");

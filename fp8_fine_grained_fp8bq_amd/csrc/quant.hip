@@ -250,6 +250,113 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Transposing re-quantisation of an FP8 activation cache (1x128 -> 128x1).
+// The report's backward step (section 3.5.2, "support for transposed GEMM"):
+// read the forward pass's FP8 codes and 1x128 scales, dequantise, transpose
+// and quantise again into 128x1 tiles; for these activations every scale is an
+// integral power of two (section 3.3.3), so the conversion adds no error of its
+// own where the row scale is not below the new one.
+// x_hat = dec(q) * s is formed in float64, where it is exact for any binary32
+// scale (4 + 24 significant bits); the new scale is 2^k with k the smallest
+// exponent such that the 128x1 group's absmax is at most 448 * 2^k (E8M0
+// range, 2^-127 for an all-zero group); the code is E4M3(fl32(x_hat * 2^-k)),
+// the product exact in float64 and rounded once to binary32.
+// One 256-thread block per 128 x 128 block of the cache: the codes are staged
+// in LDS; thread (p, seg) takes columns 4p .. 4p + 3 of rows 16 seg .. 16 seg +
+// 15, so each of its four output rows gets 16 consecutive bytes; the column
+// maxima meet across the 8 lanes that share p.
+// ---------------------------------------------------------------------------
+constexpr int kReqStride = 33;   // dwords per staged row of 128 codes (+1 pad)
+
+// The four E4M3 codes of a word as floats (exact; hardware conversion).
+__device__ __forceinline__ void dec4(uint32_t w, float (&f)[4]) {
+  f[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  f[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  f[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
+
+__device__ __forceinline__ double dmax_lane8(double v) {
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) v = fmax(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// k = smallest integer with a <= 448 * 2^k, clamped to [-127, 127]; a >= 0.
+__device__ __forceinline__ int pow2_exponent_f64(double a) {
+  const uint64_t b = (uint64_t)__double_as_longlong(a);
+  const int e = (int)((b >> 52) & 0x7FF);
+  const uint64_t m = b & 0xFFFFFFFFFFFFFull;
+  const int k = e - 1031 + (m > 0xC000000000000ull ? 1 : 0);   // 448 = 1.75 * 2^8
+  return max(-127, min(127, k));
+}
+
+__global__ __launch_bounds__(256) void requant_t_kernel(
+    const uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
+  __shared__ uint32_t tile[128 * kReqStride];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = i * 32 + (t >> 3);
+    const uint4 w = *reinterpret_cast<const uint4*>(q + (r0 + row) * ldq + c0 + (t & 7) * 16);
+    uint32_t* dst = tile + row * kReqStride + (t & 7) * 4;
+    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+  }
+  const int p = t >> 3, seg = t & 7;
+  const float* srow = s + (int64_t)blockIdx.x * lds + r0 + seg * 16;
+  float sf[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sf[i] = srow[i];
+  __syncthreads();
+
+  // pass 1: the column maxima of |x_hat|; pass 2 forms x_hat again (cheaper
+  // than keeping 64 float64 values live)
+  uint32_t w[16];
+  double cmax[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    w[i] = tile[(seg * 16 + i) * kReqStride + p];
+    float d[4];
+    dec4(w[i], d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cmax[b] = fmax(cmax[b], fabs((double)d[b] * (double)sf[i]));   // exact
+  }
+  int k[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) k[b] = pow2_exponent_f64(dmax_lane8(cmax[b]));
+
+  float v[4][16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float d[4];
+    dec4(w[i], d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b][i] = (float)ldexp((double)d[b] * (double)sf[i], -k[b]);   // exact, one rounding
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint4 o;
+    o.x = cvt4(v[b][0], v[b][1], v[b][2], v[b][3]);
+    o.y = cvt4(v[b][4], v[b][5], v[b][6], v[b][7]);
+    o.z = cvt4(v[b][8], v[b][9], v[b][10], v[b][11]);
+    o.w = cvt4(v[b][12], v[b][13], v[b][14], v[b][15]);
+    *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldqt + r0 + seg * 16) = o;
+  }
+  if (seg == 0) {
+    float4 sc;
+    float* scp = reinterpret_cast<float*>(&sc);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      scp[b] = k[b] >= -126 ? __uint_as_float((uint32_t)(k[b] + 127) << 23) : __uint_as_float(0x00400000u);
+    float* sp = st + (int64_t)blockIdx.y * ldst + c0 + 4 * p;
+    sp[0] = sc.x; sp[1] = sc.y; sp[2] = sc.z; sp[3] = sc.w;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 128x128 weight blocks. One 256-thread block per weight block: each thread
 // holds 64 elements (8 rows x 8 columns) in registers, so the block is read
 // from HBM once; the absmax goes DPP row -> cross-row shuffles -> LDS.
@@ -340,6 +447,13 @@ hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, 
     hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
   else
     hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                            int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream) {
+  dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+  hipLaunchKernelGGL(requant_t_kernel, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
   return hipGetLastError();
 }
 

@@ -104,6 +104,33 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
                           void* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
 /*
+ * Transposing re-quantisation of an FP8 activation cache, 1x128 -> 128x1
+ * (report section 3.5.2 "support for transposed GEMM": the forward pass keeps
+ * activations as 1x128 FP8 tiles, the backward pass reads them, dequantises,
+ * transposes and quantises them again as 128x1 tiles; section 3.3.3 gives
+ * these activations power-of-two scales so the conversion adds no error of
+ * its own).
+ *
+ * q     E4M3 [rows, cols], ldq >= cols, as written by fp8bq_quant_act_1x128
+ *       in ROWWISE mode (any scales: the dequantised value dec(q) * s is
+ *       formed exactly).
+ * s     float, tile (r, c) at s[c * lds + r], lds >= rows.
+ * qt    E4M3 [cols, rows], ldqt >= rows: qt[j * ldqt + r] encodes column j,
+ *       row r (the layout of COLWISE mode, ready to be a Wgrad operand).
+ * st    float, power-of-two scale of tile (rows [128c, 128c+128), column j)
+ *       at st[c * ldst + j], ldst >= cols: 2^k with k the smallest integer
+ *       such that the tile's absmax <= 448 * 2^k, within [-127, 127] (2^-127
+ *       for an all-zero tile); codes are E4M3(fl32(x_hat * 2^-k)).
+ * flags must be 0. rows and cols must be multiples of 128.
+ * The caller owns all buffers; q/s and qt/st must not overlap.
+ * Errors: E_INVAL (null, sizes <= 0, ld too small, flags), E_SHAPE,
+ *         E_ALIGN (q, qt 16-byte aligned; ldq, ldqt multiples of 16; scales
+ *         4-byte aligned), E_DEVICE, E_HIP.
+ */
+int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
+                          void* qt, int64_t ldqt, float* st, int64_t ldst, int flags, void* stream);
+
+/*
  * Online weight quantisation with 128x128 blocks (report section 3.3.2,
  * Figure 7a: per 128 input channels x 128 output channels).
  *

@@ -34,8 +34,8 @@ def _declared():
 
 def test_header_declares_the_four_entry_points():
     d = _declared()
-    for name in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_gemm", "fp8bq_grouped_gemm",
-                 "fp8bq_last_error"):
+    for name in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
+                 "fp8bq_grouped_gemm", "fp8bq_last_error"):
         assert name in d
 
 
@@ -81,6 +81,27 @@ def test_quant_w_validation(L):
     assert _st(L, f, *ok[:4] + [B16 + 8] + ok[5:]) == fb.E_ALIGN
     assert _st(L, f, *ok[:10] + [0x20, None]) == fb.E_INVAL                     # unknown flag
     assert "flags" in L.fp8bq_last_error().decode()
+
+
+def test_requant_validation(L):
+    f = "fp8bq_requant_t_128x1"
+    # rows, cols = 256, 384: q [256, 384] ldq 384, s lds 256, qt [384, 256] ldqt 256, st ldst 384
+    ok = [A16, 256, 384, 384, S4, 256, B16, 256, S4 + 4096, 384, 0, None]
+    def bad(i, v):
+        a = list(ok); a[i] = v
+        return _st(L, f, *a)
+    assert bad(0, None) == fb.E_INVAL
+    assert bad(10, 1) == fb.E_INVAL and "flags" in L.fp8bq_last_error().decode()
+    assert bad(1, 0) == fb.E_INVAL
+    assert bad(1, 200) == fb.E_SHAPE
+    assert bad(2, 300) == fb.E_SHAPE
+    assert bad(3, 256) == fb.E_INVAL                                            # ldq < cols
+    assert bad(5, 128) == fb.E_INVAL                                            # lds < rows
+    assert bad(7, 128) == fb.E_INVAL                                            # ldqt < rows
+    assert bad(9, 256) == fb.E_INVAL                                            # ldst < cols
+    assert bad(6, B16 + 8) == fb.E_ALIGN
+    assert bad(3, 392) == fb.E_ALIGN                                            # ldq % 16
+    assert bad(8, S4 + 2) == fb.E_ALIGN
 
 
 def _gemm_ok(op=0):
