@@ -30,18 +30,25 @@ How the oracle evaluates it:
 * G3. y64 = sum_c P_c * s_A * s_B in float64, and the tolerance scale
   absbound = sum_k |x_hat_k| * |w_hat_k| (= sum_c s_A s_B sum_k |qA||qB|).
 * G4. The BF16 epilogue is round-to-nearest-even of y32.
+* G5. Producer fusion (report section 3.5.2, "online quantization support":
+  activations are read from HBM, quantised, written back and read again for
+  the next matrix multiply, which fusing the cast into the producer saves):
+  the BF16 output of G4 quantised at once as the next GEMM's activation
+  operand, 1x128 tiles along each row (oracle.quant.quant_act_1x128). Reading:
+  the tiles are quantised from the BF16 values the GEMM would store.
 
 Pinned by: tests/test_oracle_gemm.py -- P_c against an exact integer dot of
 the codes; tiny shapes against a Fraction triple loop; y64 against the plain
 product of the dequantised operands; the uniform-scale special case (textbook
-per-tensor-scaled FP8 GEMM); K = 128; the bf16 epilogue against torch.
+per-tensor-scaled FP8 GEMM); K = 128; the bf16 epilogue against torch; G5
+against exact fractions and the exhaustive encoder on a tiny GEMM.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, quant
 
 CHUNK = 128
 
@@ -132,3 +139,12 @@ def bf16_rne_bits(y32: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact value of bf16 bit patterns."""
     return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def quantise_output(y32: np.ndarray, scale_mode: str = "exact") -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """G5: the GEMM's BF16 output (G4) as the next GEMM's FP8 activation operand.
+
+    Returns (bf16 bits [M, N], codes uint8 [M, N], scales float32 [M, N/128])."""
+    bits = bf16_rne_bits(y32)
+    q, s = quant.quant_act_1x128(bits, scale_mode)
+    return bits, q, s

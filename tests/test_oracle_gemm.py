@@ -162,3 +162,72 @@ def test_fp32_accumulation_bound(seed):
     y32, y64, ab = gemm.fprop(qx, sx, qw, sw)
     nc = 1024 // 128
     assert np.all(np.abs(y32.astype(np.float64) - y64) <= (2 * nc + 1) * 2.0 ** -24 * ab)
+
+
+def _fl32(f: Fraction) -> float:
+    """Binary32 round-to-nearest-even of an exact rational (normal range)."""
+    if f == 0:
+        return 0.0
+    sign = -1 if f < 0 else 1
+    f = abs(f)
+    e = f.numerator.bit_length() - f.denominator.bit_length()
+    while Fraction(2) ** e > f:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= f:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = f / ulp
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * float(lo * ulp)
+
+
+@pytest.mark.parametrize("mode", ["exact", "pow2"])
+def test_quantise_output_against_fractions(mode):
+    # G5 on a tiny GEMM whose output is exact (small codes, power-of-two scales):
+    # y from a Fraction triple loop, its bf16 rounding from torch, then per
+    # 1x128 row tile the scale (fl32(amax / 448) rounded exactly from the
+    # fraction, or the smallest power of two 2^k with amax <= 448 * 2^k) and
+    # every code from the exhaustive nearest-value encoder
+    from workloads import pow2_scales, small_codes
+    qa = small_codes(71, 3, 256)
+    qa[1] = 0                                            # a zero row: scale 0 / 2^-127, codes +0
+    qb = small_codes(72, 256, 256)
+    sa = pow2_scales(73, (3, 2))
+    sb = pow2_scales(74, (2, 2))
+    y32, _, _ = gemm.fprop(qa, sa, qb, sb)
+    bits, q, s = gemm.quantise_output(y32, mode)
+    da, db = e4m3.decode(qa), e4m3.decode(qb)
+    for i in range(3):
+        for g in range(2):
+            ys = []
+            for j in range(128 * g, 128 * g + 128):
+                v = sum(Fraction(float(da[i, k])) * Fraction(float(db[j, k])) * Fraction(float(sa[i, k // 128]))
+                        * Fraction(float(sb[j // 128, k // 128])) for k in range(256))
+                assert float(y32[i, j]) == v                 # the output is exact
+                ys.append(v)
+            yb = torch.tensor([float(v) for v in ys], dtype=torch.float32).to(torch.bfloat16)
+            np.testing.assert_array_equal(bits[i, 128 * g:128 * g + 128],
+                                          yb.view(torch.int16).numpy().view(np.uint16))
+            yv = [Fraction(float(v)) for v in yb.float().numpy()]
+            amax = max(abs(v) for v in yv)
+            if mode == "pow2":
+                k = -127
+                while amax > 448 * Fraction(2) ** k:
+                    k += 1
+                want_s = 2.0 ** k
+                vals = [v / Fraction(2) ** k for v in yv]
+            else:
+                want_s = _fl32(amax / 448) if amax else 0.0
+                vals = [Fraction(_fl32(v / Fraction(want_s))) if want_s else Fraction(0) for v in yv]
+            assert float(s[i, g]) == want_s
+            want_q = e4m3.encode_bruteforce_vec(np.array([float(v) for v in vals]))
+            np.testing.assert_array_equal(q[i, 128 * g:128 * g + 128], want_q)
+    # planted mistake: tiles of the fp32 output instead of its bf16 rounding
+    # would give other exact scales on this input, which the checks above reject
+    if mode == "exact":
+        am = np.abs(y32.reshape(3, 2, 128).astype(np.float64)).max(-1)
+        s_f32 = (am / 448).astype(np.float32)
+        assert not np.array_equal(s_f32[s_f32 > 0], s[s > 0])

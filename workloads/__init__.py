@@ -135,3 +135,23 @@ def moe_fprop(seed: int = 1004, tokens: int = 16384, n: int = 2048, k: int = 716
     w = np.stack([f32_to_bf16_bits(_normal(rw, (n, k), 0.02)) for _ in range(local)])
     return MoE(f"MoE grouped fprop {local} experts, {tokens} tokens top-8, N={n} K={k}",
                x, w, row_off, counts)
+
+
+# E4M3 byte patterns of 0, +-0.5, +-1, +-1.5, +-2, +-3, +-4. A product of two of
+# these is a multiple of 1/4 below 16 in magnitude, so a block-scaled GEMM over
+# such codes with power-of-two scales near 1 is exact in fp32 (every partial
+# sum is a short dyadic number): its output, and therefore the bf16 rounding of
+# it, has one right answer.
+SMALL_CODES = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0xB0, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8], np.uint8)
+
+
+def small_codes(seed: int, rows: int, cols: int) -> np.ndarray:
+    """uint8 [rows, cols] drawn from SMALL_CODES."""
+    rng = np.random.default_rng(seed)
+    return SMALL_CODES[rng.integers(0, SMALL_CODES.size, (rows, cols))]
+
+
+def pow2_scales(seed: int, shape, lo: int = -1, hi: int = 1) -> np.ndarray:
+    """float32 powers of two 2^e, e uniform in [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    return np.ldexp(np.float32(1.0), rng.integers(lo, hi + 1, shape).astype(np.int32)).astype(np.float32)
