@@ -76,7 +76,7 @@ def gemm_traffic():
     changed since the counters were taken (or the summary is missing)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "large_fprop_hbm_traffic.md")
-    src = os.path.join(ROOT, "fp8_fine_grained_fp8bq_amd", "csrc", "gemm.hip")
+    src = os.path.join(ROOT, "fp8_fine_grained_fp8bq_amd", "csrc", "gemm_kernels.h")
     try:
         kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith("gemm_") and ": " in line)

@@ -8,13 +8,14 @@ fallback: if the library is missing or the device is not gfx950, calls raise.
 
 Two layers with the C names:
 
-* `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_gemm`,
-  `fp8bq_grouped_gemm`: pointer-level, exactly the C signatures (ints for
-  pointers and the stream); a non-zero status raises `Fp8bqError`.
-* `quant_act_1x128`, `quant_w_128x128`, `gemm`, `grouped_gemm`: take torch
-  tensors on the GPU, allocate the outputs with torch (memory and streams are
-  the only things torch provides) and call the same entry points on the
-  current stream.
+* `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
+  `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`: pointer-level,
+  exactly the C signatures (ints for pointers and the stream); a non-zero
+  status raises `Fp8bqError`.
+* `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
+  `gemm_quant`, `grouped_gemm`: take torch tensors on the GPU, allocate the
+  outputs with torch (memory and streams are the only things torch provides)
+  and call the same entry points on the current stream.
 """
 
 from __future__ import annotations
@@ -32,7 +33,7 @@ ACT_ROWWISE, ACT_COLWISE = 0, 1
 SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-           "fp8bq_grouped_gemm", "fp8bq_last_error", "fp8bq_version")
+           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_last_error", "fp8bq_version")
 
 
 class Fp8bqError(RuntimeError):
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         L.fp8bq_requant_t_128x1.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, fp, i64, i32, vp]
         L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
+        L.fp8bq_gemm_quant.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64,
+                                       vp, i64, fp, i64, i32, vp]
         L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
                                          vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
@@ -98,6 +101,13 @@ def fp8bq_requant_t_128x1(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, flags=
 def fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream=0):
     return _check("fp8bq_gemm",
                   lib().fp8bq_gemm(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, stream))
+
+
+def fp8bq_gemm_quant(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, q, ldq, s, lds, qflags=0,
+                     stream=0):
+    return _check("fp8bq_gemm_quant",
+                  lib().fp8bq_gemm_quant(op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, q, ldq, s, lds,
+                                         qflags, stream))
 
 
 def fp8bq_grouped_gemm(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, flags=0,
@@ -194,6 +204,23 @@ def gemm(op: int, a, sa, b, sb, out=None):
                b.data_ptr(), b.stride(0), sb.data_ptr(), sb.stride(0), out.data_ptr(), out.stride(0),
                _stream(a))
     return out
+
+
+def gemm_quant(op: int, a, sa, b, sb, with_out: bool = True, qpow2: bool = False):
+    """fp8bq_gemm (FPROP / DGRAD, `op` may include SCALE_POW2) that also quantises its bf16
+    output in 1x128 tiles. Returns (out bf16 [m, n] or None, q uint8 [m, n], s float32
+    [n/128, m]); qpow2 selects power-of-two output scales."""
+    import torch
+    m, k = a.shape
+    n = b.shape[0]
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device) if with_out else None
+    q = torch.empty((m, n), dtype=torch.uint8, device=a.device)
+    s = torch.empty((n // 128, m), dtype=torch.float32, device=a.device)
+    fp8bq_gemm_quant(op, m, n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
+                     b.data_ptr(), b.stride(0), sb.data_ptr(), sb.stride(0),
+                     out.data_ptr() if out is not None else None, n, q.data_ptr(), n, s.data_ptr(), m,
+                     SCALE_POW2 if qpow2 else 0, _stream(a))
+    return out, q, s
 
 
 def grouped_gemm(row_off, a, sa, b, sb, out=None, pow2: bool = False):

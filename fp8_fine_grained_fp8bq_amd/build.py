@@ -15,11 +15,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8bq.so")
 
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "gemm_quant.hip", "gemm_grouped.hip"]
 
 # -packed-fp32-ops: no packed FP32 VALU instructions (v_pk_*_f32) in any kernel.
 # -Wno-inline-asm: the LDS-DMA helpers name M0 (a compiler-reserved register) as
-# clobbered on purpose; see gemm.hip.
+# clobbered on purpose; see gemm_kernels.h.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -35,16 +35,34 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libfp8bq.so (always recompiles)."""
+    """Compile every source into libfp8bq.so (always recompiles). The sources
+    compile in parallel to objects, which are then linked."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    procs = []
+    for f in SOURCES:
+        obj = os.path.join(objdir, f + ".o")
+        cmd = [hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, f), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((f, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for f, _, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(f)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, f) for f in SOURCES], "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[obj for _, obj, _ in procs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -181,6 +181,37 @@ int fp8bq_gemm(int op_flags, int64_t m, int64_t n, int64_t k, const void* a, int
                                      reinterpret_cast<hipStream_t>(stream)), "gemm");
 }
 
+int fp8bq_gemm_quant(int op_flags, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                     const float* sa, int64_t ldsa, const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                     void* out, int64_t ldo, void* q, int64_t ldq, float* s, int64_t lds, int qflags,
+                     void* stream) {
+  const bool pow2 = (op_flags & FP8BQ_SCALE_POW2) != 0;
+  const int op = op_flags & ~FP8BQ_SCALE_POW2;
+  if (op != FP8BQ_FPROP && op != FP8BQ_DGRAD)
+    return fail(FP8BQ_E_INVAL, "gemm_quant: op must be FPROP (0) or DGRAD (1), optionally | SCALE_POW2, got %d",
+                op_flags);
+  if (qflags & ~FP8BQ_SCALE_POW2) return fail(FP8BQ_E_INVAL, "gemm_quant: unknown qflags %d", qflags);
+  if (!q || !s) return fail(FP8BQ_E_INVAL, "gemm_quant: null q or s");
+  // the bf16 output is optional: validate it when given, else the checks run on q
+  if (int st = check_gemm_common("gemm_quant", m, n, k, a, lda, sa, b, ldb, sb, out ? out : q,
+                                 out ? ldo : n, 2))
+    return st;
+  if (ldsa < m) return fail(FP8BQ_E_INVAL, "gemm_quant: ldsa must be >= m");
+  if (op == FP8BQ_FPROP && ldsb < k / 128) return fail(FP8BQ_E_INVAL, "gemm_quant: FPROP ldsb must be >= k / 128");
+  if (op == FP8BQ_DGRAD && ldsb < n / 128) return fail(FP8BQ_E_INVAL, "gemm_quant: DGRAD ldsb must be >= n / 128");
+  if (ldq < n) return fail(FP8BQ_E_INVAL, "gemm_quant: ldq must be >= n");
+  if (lds < m) return fail(FP8BQ_E_INVAL, "gemm_quant: lds must be >= m");
+  if (!aligned(q, 16) || ldq % 16 || !aligned(s, 4))
+    return fail(FP8BQ_E_ALIGN, "gemm_quant: q must be 16-byte aligned with ldq a multiple of 16, s 4-byte aligned");
+  if (int st = check_device()) return st;
+  return launched(fp8bq::launch_gemm_quant(op, m, n, k, static_cast<const uint8_t*>(a), lda, sa, ldsa,
+                                           static_cast<const uint8_t*>(b), ldb, sb, ldsb,
+                                           static_cast<uint16_t*>(out), ldo, static_cast<uint8_t*>(q), ldq, s, lds,
+                                           pow2, (qflags & FP8BQ_SCALE_POW2) != 0,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  "gemm_quant");
+}
+
 int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
                        int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
                        const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags, void* stream) {

@@ -1,867 +1,8 @@
-// Block-scaled FP8 GEMM with per-128-K-chunk promotion into FP32, for gfx950.
-//
-//   out[i][j] = sum_c P_c[i][j] * sa(i, c) * sb(j, c),
-//   P_c[i][j] = sum_{k in chunk c} a[i][k] * b[j][k]     (E4M3 x E4M3, exact products)
-//
-// This is the FP8 GEMM of the DeepSeek-V3 report (Chinese translation), section
-// 3.3.2 "increasing accumulation precision" and Figure 7b: every N_C = 128
-// K-elements the matrix-core partial sum is promoted to FP32 registers, where
-// it is multiplied by both operands' group scales and added (the tech note
-// "DeepSeek-V3 FP8 dynamic quantisation": out += MMA(FP8 x, FP8 w) * s_x * s_w).
-// On the pages' hardware the promotion moves partial sums from tensor cores to
-// CUDA cores; on CDNA4 the MFMA writes its result straight into VGPRs, so the
-// "promotion" is one VALU FMA per output per chunk into a second accumulator.
-//
-// Design (MI355X / gfx950):
-//  * One v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-K chunk of a 16x16
-//    tile, so each chunk's partial sum is a fresh MFMA result (C = 0) that is
-//    folded into the FP32 accumulator with acc = fma(P, scale, acc).
-//  * The weight tile is the MFMA's first operand and the activation tile its
-//    second, so a lane's four result registers are four consecutive output
-//    columns j of one output row i: one activation scale per (lane, 16-row
-//    subtile) per chunk and 8-byte (bf16) / 16-byte (fp32) output stores.
-//  * Workgroup tile 256 x 256, 8 waves (two per SIMD) of 64 x 128: 128
-//    accumulator VGPRs per lane (the promotion FMAs need the accumulator in the
-//    256 VGPRs the VALU can address, which rules out 128 x 128 wave tiles),
-//    24 KB of LDS operand reads per wave per chunk.
-//  * Operands stream global -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), two 66 KB stages (A 32 KB, B 32 KB, scales 2 KB), one barrier
-//    per chunk; the next chunk's loads run under the current chunk's MFMAs.
-//  * LDS rows are 128 bytes (one chunk); the 16-byte slot s of row r is stored
-//    at slot s ^ (r & 7) ^ ((r >> 3) & 1). An operand read has 16 lanes on 16
-//    consecutive rows at one logical slot; measured on gfx950, ds_read_b128
-//    runs at full LDS bandwidth only if rows r and r + 8 also land in different
-//    slots (an (r & 7) swizzle alone halves it).
-//  * Persistent workgroups, one per CU; each XCD (own L2) walks a contiguous
-//    range of output tiles in groups of 8 row-tiles, so the blocks resident on
-//    one XCD share activation and weight panels in its L2. The next tile's
-//    first chunk is fetched during the current tile's last chunk.
-#include "internal.h"
+// Launcher of the block-scaled FP8 GEMM (fp8bq_gemm): the VALU-promotion
+// kernel for general scales, the scaled-MFMA kernel for power-of-two scales.
+#include "gemm_kernels.h"
 
 namespace fp8bq {
-namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kABytes = BM * BK;
-constexpr int kBBytes = BN * BK;
-constexpr int kSaOff = kABytes + kBBytes;
-constexpr int kSbOff = kSaOff + BM * 4;
-constexpr int kStage = kSbOff + BN * 4;
-constexpr int kGroupM = 8;
-constexpr int kXcds = 8;
-
-template <int WAVES_M, int WAVES_N>
-struct Cfg {
-  static constexpr int kWaves = WAVES_M * WAVES_N;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int WM = BM / WAVES_M;
-  static constexpr int WN = BN / WAVES_N;
-  static constexpr int TM = WM / 16;
-  static constexpr int TN = WN / 16;
-  static_assert(WN == 128, "one weight block column per wave");
-  static_assert(BM == BN, "square workgroup tile");
-};
-
-struct GemmArgs {
-  int64_t m, n, k;
-  const uint8_t* a; int64_t lda;
-  const float* sa; int64_t ldsa;
-  const uint8_t* b; int64_t ldb;
-  const float* sb; int64_t ldsb;
-  void* out; int64_t ldo;
-  int tiles_m, tiles_n;
-};
-
-struct GroupArgs {
-  int groups;
-  int tile_prefix[kMaxGroups + 1];   // first row-tile of each group
-  int row_off128[kMaxGroups + 1];    // row offsets in units of 128 rows
-};
-
-// Global -> LDS DMA (gfx950 global_load_lds_dword[x4]): lane i's bytes land at
-// M0 + i * size. Issued from inline asm so that the compiler does not guard
-// every later LDS read with a wait for these loads; the kernel waits itself
-// (vmcnt(0) + barrier before a stage is read). Every vector memory load in the
-// K-loop goes through these helpers, so vmcnt counts exactly them.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// M0 is reserved by the compiler; on gfx950 only LDS DMA reads it and the
-// compiler itself never keeps a value there across these statements (the
-// build passes -Wno-inline-asm for this clobber).
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
-}
-// The same 16-byte LDS DMA through a raw buffer resource (base, byte bound):
-// a lane whose offset (VGPR, no scalar offset, no thread-id addressing) is at
-// or past the bound reads nothing from memory and its bytes come back as
-// zeros.
-__device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
-}
-// Raw buffer resource over [base, end) (bound capped at 4 GiB - 1: offsets
-// stay below 2 GiB), all words uniform.
-__device__ __forceinline__ u32x4 make_rsrc(const uint8_t* base, const uint8_t* end) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t n = end > base ? (uint64_t)(end - base) : 0;
-  u32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);   // stride 0: raw
-  r.z = __builtin_amdgcn_readfirstlane(n > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)n);
-  r.w = 0x00020000u;
-  return r;
-}
-// Moves a resource's base on by d bytes (d below its bound).
-__device__ __forceinline__ void bump_rsrc(u32x4& r, uint32_t d) {
-  const uint64_t b = (((uint64_t)r.y << 32) | r.x) + d;
-  r.x = (uint32_t)b;
-  r.y = (uint32_t)(b >> 32);
-  r.z = r.z == 0xFFFFFFFFu ? r.z : r.z - d;
-}
-
-// A pointer every lane holds the same value of, moved to scalar registers
-// (the LDS-DMA helpers take their base address in SGPRs).
-template <class T>
-__device__ __forceinline__ T* uniform_ptr(T* ptr) {
-  const uint64_t v = (uint64_t)(uintptr_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Physical-slot XOR of LDS row r (see the layout note at the top).
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-__device__ __forceinline__ v8i frag(const uint8_t* rowp, int off0, int off1) {
-  const uint4 x0 = *reinterpret_cast<const uint4*>(rowp + off0);
-  const uint4 x1 = *reinterpret_cast<const uint4*>(rowp + off1);
-  return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-}
-
-// Folds one chunk's MFMA result into the FP32 accumulator with the chunk's
-// scales: acc += P * (s_a * s_b). FPROP / DGRAD pass the product of the row's
-// activation scale and the weight block scale in sc; WGRAD has a row scale per
-// output row (sc) and a column scale per output column (sbj).
-// The empty asm pins the fold where it is written: without it the compiler
-// sinks the folds of a whole chunk below the mid-chunk barrier, keeping every
-// MFMA result of the chunk live at once.
-template <int KIND>
-__device__ __forceinline__ void fold(v4f& acc, const v4f& pc, float sc, const v4f& sbj) {
-  if constexpr (KIND == KIND_WGRAD) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pc[r] * sbj[r], sc, acc[r]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pc[r], sc, acc[r]);
-  }
-  asm volatile("" : "+v"(acc));
-}
-
-// One output tile: its row / column ranges and the weight (with scales) it uses.
-struct Tile {
-  int64_t m0, m_end, n0, n_end;
-  const uint8_t* b;
-  const float* sb;
-};
-
-template <bool GROUPED>
-__device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g, int logical) {
-  const int per_group = kGroupM * p.tiles_n;
-  const int group = logical / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(p.tiles_m - first_m, kGroupM);
-  const int in_group = logical - group * per_group;
-  const int tmi = first_m + in_group % gsize;
-  const int tni = in_group / gsize;
-  Tile t;
-  t.b = p.b;
-  t.sb = p.sb;
-  if constexpr (GROUPED) {
-    int lo = 0, hi = g.groups;             // find e: tile_prefix[e] <= tmi < tile_prefix[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (g.tile_prefix[mid] <= tmi) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    t.m0 = (int64_t)g.row_off128[e] * 128 + (int64_t)(tmi - g.tile_prefix[e]) * BM;
-    t.m_end = min(t.m0 + BM, (int64_t)g.row_off128[e + 1] * 128);
-    t.b += (int64_t)e * p.n * p.ldb;
-    t.sb += (int64_t)e * (p.n / 128) * p.ldsb;
-    // the group table is read with scalar loads, which complete out of order
-    // with LDS reads: wait for them here, or every later LDS wait the compiler
-    // places would have to wait for everything
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-  } else {
-    t.m0 = (int64_t)tmi * BM;
-    t.m_end = min(t.m0 + BM, p.m);
-  }
-  t.n0 = (int64_t)tni * BN;
-  t.n_end = min(t.n0 + BN, p.n);
-  return t;
-}
-
-// This workgroup's share of the persistent tile walk. Workgroup w runs on XCD
-// w % 8 (hardware round-robin); the tiles of XCD x are a contiguous range of
-// the grouped walk, shared out among that XCD's workgroups, so blocks resident
-// on one XCD (one L2) work on neighbouring tiles. Its tiles are logical
-// indices start + local + nper * t, t = 0 .. my_tiles - 1.
-struct Walk {
-  int start, local, nper, my_tiles, nc, total;
-};
-
-__device__ __forceinline__ Walk make_walk(const GemmArgs& p) {
-  Walk wk;
-  const int G = gridDim.x, w = blockIdx.x;
-  const int T = p.tiles_m * p.tiles_n;
-  const int x = w % kXcds;
-  wk.local = w / kXcds;
-  wk.nper = G / kXcds + (x < G % kXcds ? 1 : 0);
-  const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
-  wk.start = x * (T / kXcds) + min(x, T % kXcds);
-  wk.my_tiles = wk.local < count ? (count - wk.local + wk.nper - 1) / wk.nper : 0;
-  wk.nc = (int)(p.k / BK);
-  wk.total = wk.my_tiles * wk.nc;
-  return wk;
-}
-
-// ---- epilogue ----------------------------------------------------------------
-// Stores a wave's TM x TN subtiles (lane: output row l16 of subtile i, columns
-// 4 lq .. 4 lq + 3 of subtile j) as bf16 (round to nearest even, hardware
-// v_cvt_pk_bf16_f32, equal to the integer rounding on every finite fp32) or
-// fp32. Full tiles take one row pointer per subtile row and constant column
-// offsets; edge tiles check every row and column.
-template <int KIND, int TM, int TN>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
-                                           int64_t row0, int64_t col0) {
-  auto put = [&](int64_t row, int64_t col, const v4f& v) {
-    if constexpr (KIND == KIND_WGRAD) {
-      *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + row * p.ldo + col) = v;
-    } else {
-      const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-      const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-      uint2 packed;
-      __builtin_memcpy(&packed.x, &lo, 4);
-      __builtin_memcpy(&packed.y, &hi, 4);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col) = packed;
-    }
-  };
-  if (cur.m_end - cur.m0 == BM && cur.n_end - cur.n0 == BN) {   // uniform
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        if (row0 + i * 16 < cur.m_end && col0 + j * 16 < cur.n_end) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
-  }
-}
-
-// ---- global -> LDS loads ----------------------------------------------------
-// Loader wave w (w < LOADERS) fills, in round i, tile rows
-// i * kRowsPerRound + 8 w + ln / 8 (lane ln), 16 bytes at physical slot
-// ln % 8, i.e. logical slot (ln % 8) ^ swz(row); with an even number of
-// loaders swz(row) = (ln / 8) ^ (w & 1) in every round, so a lane's slot is
-// fixed and only its row moves. The lane's byte offset from the tile's first
-// row in each round is the same for every step and every tile, so it is
-// computed once; the operand tiles are read through raw buffer resources whose
-// base is the step's chunk of the tile's first row and whose bound is the end
-// of the operand, so rows past the end read as zeros (their results are never
-// stored). Offsets are 32-bit (the host checks that 256 rows of either operand
-// span less than 2 GiB).
-// Scales are brought by eight "scale waves" of 64 lanes (each real wave plays
-// 8 / WAVES of them): scale waves 0-3 bring 64 activation scales each; 4-7
-// bring 64 column scales each (WGRAD), or scale wave 4 brings the tile's two
-// weight block scales (lane 0 the first block, lane 1 the second, which is the
-// first again when the tile has only one).
-//
-// The cursor (dtk, dc) is the next step to load: step s is chunk s % nc of the
-// workgroup's (s / nc)-th tile and lives in stage s % 2; rs_a, rs_b and d_sk
-// address its chunk of A, B and the scale vectors. A step goes out as kParts load
-// instructions per wave, part(0 .. kParts-1), and then advance() moves the
-// cursor on. After the last step the cursor stays put: further loads repeat
-// that step into a stage no one reads any more (the kernels wait for them
-// before they end), which keeps every load unconditional.
-template <int KIND, bool GROUPED, int WAVES, int LOADERS>
-struct Loader {
-  static constexpr int kRowsPerRound = 8 * LOADERS;      // one dwordx4 load per wave covers 8 rows
-  static constexpr int kRounds = BM / kRowsPerRound;
-  static constexpr int kScaleWaves = 8 / WAVES;
-  static constexpr int kParts = 2 * kRounds + kScaleWaves;
-  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0, "load rounds");
-  static_assert(WAVES == 4 || WAVES == 8, "scale waves");
-
-  const GemmArgs& p;
-  const GroupArgs& g;
-  const Walk& wk;
-  const uint32_t smem_base;
-  const int wave, lane;
-  const uint32_t lrow, g16;
-  uint32_t voff_a[kRounds], voff_b[kRounds];
-  uint32_t s_off[kScaleWaves];
-  int64_t s_step[kScaleWaves];
-  const float* d_sk[kScaleWaves];
-  u32x4 rs_a, rs_b;
-  int dtk = 0, dc = 0;
-
-  __device__ __forceinline__ Loader(const GemmArgs& p_, const GroupArgs& g_, const Walk& wk_, uint32_t smem_base_,
-                                    int wave_, int lane_)
-      : p(p_), g(g_), wk(wk_), smem_base(smem_base_), wave(wave_), lane(lane_),
-        lrow(8 * wave_ + (lane_ >> 3)), g16((uint32_t)(((lane_ & 7) ^ (lane_ >> 3) ^ (wave_ & 1)) * 16)) {
-#pragma unroll
-    for (int v = 0; v < kScaleWaves; ++v) {
-      // per-step advance of a scale pointer: activation scales are chunk-major;
-      // FPROP block scales are contiguous along K, DGRAD's and the WGRAD column
-      // scales chunk-major
-      const int sw = wave + v * WAVES;
-      s_step[v] = sw < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
-    }
-#pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      voff_a[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.lda + g16;
-      voff_b[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.ldb + g16;
-    }
-    cursor_tile();
-  }
-
-  __device__ __forceinline__ void cursor_tile() {
-    const Tile t = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * dtk);
-    rs_a = make_rsrc(p.a + t.m0 * p.lda, p.a + (p.m - 1) * p.lda + p.k);
-    rs_b = make_rsrc(t.b + t.n0 * p.ldb, t.b + (p.n - 1) * p.ldb + p.k);
-#pragma unroll
-    for (int v = 0; v < kScaleWaves; ++v) {
-      const int sw = wave + v * WAVES, q4 = sw & 3;
-      if (sw < 4) {
-        s_off[v] = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
-        d_sk[v] = p.sa + t.m0;
-      } else if constexpr (KIND == KIND_WGRAD) {
-        s_off[v] = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
-        d_sk[v] = t.sb + t.n0;
-      } else {
-        const int64_t blk0 = t.n0 / 128;
-        const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
-        const int64_t bsel = lane < 1 ? 0 : blk1;
-        s_off[v] = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
-        d_sk[v] = KIND == KIND_FPROP ? t.sb + blk0 * p.ldsb : t.sb + blk0;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void advance() {
-    if (dc + 1 < wk.nc) {
-      ++dc;
-      bump_rsrc(rs_a, BK);
-      bump_rsrc(rs_b, BK);
-#pragma unroll
-      for (int v = 0; v < kScaleWaves; ++v) d_sk[v] += s_step[v];
-    } else if (dtk + 1 < wk.my_tiles) {
-      dc = 0;
-      ++dtk;
-      cursor_tile();
-    }
-  }
-
-  // Load instruction q of the cursor's step into stage st.
-  __device__ __forceinline__ void part(int q, int st) const {
-    const uint32_t base = smem_base + (uint32_t)(st * kStage);
-    if (q < 2 * kRounds) {
-      if constexpr (LOADERS < WAVES) {
-        if (wave >= LOADERS) return;
-      }
-      if (q < kRounds)
-        dma16_buf(rs_a, voff_a[q], base + (q * kRowsPerRound + 8 * wave) * BK);
-      else
-        dma16_buf(rs_b, voff_b[q - kRounds], base + kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
-      return;
-    }
-    const int v = q - 2 * kRounds, sw = wave + v * WAVES;
-    // with four waves, scale wave v of wave w is w (activations) or w + 4
-    const bool act = WAVES == 4 ? v == 0 : sw < 4;
-    if (act || KIND == KIND_WGRAD) {
-      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (act ? kSaOff : kSbOff) + 256 * (sw & 3));
-    } else if (sw == 4) {
-      // FPROP / DGRAD: the tile's two weight block scales; a load's cost
-      // follows its active lanes, so only two lanes take part
-      if (lane < 2) dma4(uniform_ptr(d_sk[v]), s_off[v], base + kSbOff);
-    }
-  }
-};
-
-// Persistent kernel with promotion on the VALU: each workgroup owns one CU and
-// walks its tiles (make_walk); the first chunk of the next tile is fetched
-// during the current tile's last chunks, so the pipeline fills once per
-// workgroup.
-template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N, int LOADERS>
-__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
-  using C = Cfg<WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave % WAVES_M;
-  const int wave_n = wave / WAVES_M;
-  const int l16 = lane & 15, lq = lane >> 4;
-
-  const Walk wk = make_walk(p);
-  if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
-  const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
-  Loader<KIND, GROUPED, C::kWaves, LOADERS> ld(p, g, wk, lds_addr(smem), wave, lane);
-  constexpr int kParts = decltype(ld)::kParts;
-
-  // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
-  // first row is a multiple of 16: row r = base + l16, logical slots 2 lq, 2 lq + 1.
-  const int sw = swz(l16);   // the subtile's first row is a multiple of 16
-  const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
-  const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
-
-  // Fragments and scales of one step, read from its stage: the wave's TM
-  // activation subtiles, the first weight subtile and the per-row scale
-  // products of the chunk.
-  auto read_scales = [&](const uint8_t* stage, float (&sc)[C::TM]) {
-    const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
-    const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
-    if constexpr (KIND != KIND_WGRAD) {
-      const float sbv = Sb[wave_n];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
-    }
-  };
-  auto wgrad_col_scales = [&](const uint8_t* stage, int j) {
-    return *reinterpret_cast<const v4f*>(stage + kSbOff + 4 * (wave_n * C::WN + j * 16 + 4 * lq));
-  };
-  auto a_frag = [&](const uint8_t* stage, int i) { return frag(stage + (wave_m * C::WM + i * 16) * BK, off0, off1); };
-  auto b_frag = [&](const uint8_t* stage, int j) {
-    return frag(stage + kABytes + (wave_n * C::WN + j * 16) * BK, off0, off1);
-  };
-
-#pragma unroll
-  for (int q = 0; q < kParts; ++q) ld.part(q, 0);
-  ld.advance();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kParts; ++q) ld.part(q, 1);
-  ld.advance();
-
-  // Weight fragments are read kBAhead columns before their MFMAs (one column
-  // for WGRAD, whose column scales take the registers). bw[0] is the current
-  // column's, bw[q] the one q columns on; the barrier precedes column kBarCol,
-  // the first whose look-ahead read falls into the next step's stage.
-  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : 3;
-  constexpr int kBarCol = C::TN - kBAhead;
-  v8i bw[kBAhead + 1];
-#pragma unroll
-  for (int q = 0; q < kBAhead; ++q) bw[q] = b_frag(smem, q);
-  v8i af[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) af[i] = a_frag(smem, i);
-  float sc[C::TM], scp[C::TM], scn[C::TM];
-  read_scales(smem, sc);
-  // The compiler tracks at most 15 outstanding LDS reads; with more in flight
-  // where a loop iteration begins it waits for all of them before the first
-  // MFMA. This wait and the one at the last column keep the count it carries
-  // into the loop below that.
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-
-  v4f acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  // MFMA results waiting to be folded: the result of the chunk's t-th MFMA
-  // (t = j * TM + i) sits in pend[t % 4] until it is folded kLag MFMAs later,
-  // so a fold never waits for the matrix core. The last kLag results of a
-  // chunk are folded during the next chunk's first MFMAs with that chunk's
-  // scales (scp), or before the epilogue at the end of a tile.
-  constexpr int kNT = C::TM * C::TN;
-  constexpr int kLag = 3;
-  static_assert(kNT % 4 == 0 && kNT > kLag, "result ring");
-  static_assert(kLag <= C::TM, "a column's folds finish within the next column");
-  v4f pend[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) pend[q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
-  v4f sbj[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-
-  // Step s: weight columns 0 .. TN-2 from stage s % 2 with fragments already in
-  // registers; then the barrier (every wave has read all of stage s % 2, and
-  // step s + 1 has landed in the other stage), the DMA of step s + 2 into
-  // stage s % 2, and the last column's MFMAs while the fragments of step s + 1
-  // are read (each activation fragment right after its last use).
-  int s = 0;
-#pragma clang loop unroll(disable)
-  for (int tk = 0; tk < my_tiles; ++tk) {
-#pragma clang loop unroll(disable)
-    for (int c = 0; c < nc; ++c, ++s) {
-      const uint8_t* stage = smem + (s & 1) * kStage;
-      const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        if (j == kBarCol) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          read_scales(nstage, scn);
-        }
-        // last column: everything read before the previous column's weight
-        // fragment has landed (read at least a column ago)
-        if (j + 1 == C::TN) __builtin_amdgcn_s_waitcnt(0xC07F | (2 << 8));
-        bw[kBAhead] = j + kBAhead < C::TN ? b_frag(stage, j + kBAhead) : b_frag(nstage, j + kBAhead - C::TN);
-        // WGRAD column scales of column j (the last column's are read before
-        // the barrier, below: after it the stage is being refilled)
-        if constexpr (KIND == KIND_WGRAD) {
-          if (j + 1 < C::TN) sbj[j & 1] = wgrad_col_scales(stage, j);
-        }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-          const int t = j * C::TM + i;
-          pend[t % 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], zero, 0, 0, 0, 0, 0, 0);
-          if (t >= kLag) {
-            const int u = t - kLag;
-            fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], sc[u % C::TM], sbj[(u / C::TM) & 1]);
-          } else {
-            const int u = t - kLag + kNT;   // previous chunk, last column
-            fold<KIND>(acc[u % C::TM][C::TN - 1], pend[u % 4], scp[u % C::TM], sbj[(C::TN - 1) & 1]);
-          }
-          if (j + 1 == C::TN) af[i] = a_frag(nstage, i);
-          // column TN-2's last MFMA: the folds of column TN-3 are done, so its
-          // slot takes the last column's scales
-          if constexpr (KIND == KIND_WGRAD) {
-            if (j + 2 == C::TN && i + 1 == C::TM) sbj[(j + 1) & 1] = wgrad_col_scales(stage, j + 1);
-          }
-          // the cursor's step into stage s % 2 (free since the barrier): its
-          // loads spread evenly over the MFMAs after the barrier, then the
-          // cursor moves on
-          {
-            constexpr int kFirst = C::TM * kBarCol;
-            constexpr int kSlots = kNT - kFirst;
-            if (t >= kFirst) {
-#pragma unroll
-              for (int q = 0; q < kParts; ++q)
-                if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
-            }
-            if (t + 1 == kNT) ld.advance();
-          }
-          // keep this order: one MFMA, the fold of the result kLag MFMAs old,
-          // then the reads due here (no result waits for the matrix core, and
-          // MFMA results never pile up in registers)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < kBAhead; ++q) bw[q] = bw[q + 1];
-      }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) { scp[i] = sc[i]; sc[i] = scn[i]; }
-    }
-
-    // ---- tile done: remaining folds (scales of the tile's last chunk, now in
-    // scp), epilogue; the next tile's first folds then add zeros ------------
-#pragma unroll
-    for (int u = kNT - kLag; u < kNT; ++u)
-      fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], sbj[(u / C::TM) & 1]);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
-    const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
-    store_tile<KIND, C::TM, C::TN>(p, cur, acc, cur.m0 + wave_m * C::WM + l16, cur.n0 + wave_n * C::WN + 4 * lq);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  // the repeated loads after the last step must land before the workgroup's
-  // LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------
-// Power-of-two scales applied by the matrix unit.
-// v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0 exponent byte per lane for
-// each operand: lane l scales row l % 16 of its operand over K-block l / 16
-// (probed on gfx950). With power-of-two scales s = 2^k the byte is the fp32
-// exponent field (k + 127; 0 for the subnormal 2^-127) and every K-block of a
-// row carries its tile's scale, so the instruction itself multiplies each
-// product by s_a * s_b — the "MMA with group scaling" the report asks hardware
-// for (section 3.5.2) — and adds the scaled chunk sum into the FP32 accumulator
-// (C = acc), which it does block by block (8 products at a time) rather than
-// with one rounding. No VALU promotion is left, so the accumulator can live in
-// the AGPRs: 128 x 128 wave tiles (256 accumulators), 4 waves (one per SIMD),
-// workgroup tile 256 x 256, the same stages, loads and tile walk as above.
-// ---------------------------------------------------------------------------
-// Position t of the row / column pass order over an n x n grid of MFMAs:
-// row 0, column 0 (what is left of it), row 1, column 1, ...; end_a / end_b
-// name the operand whose last use this is (-1 if none).
-struct PassCell { int i, j, end_a, end_b; };
-constexpr PassCell pass_cell(int t, int n) {
-  int pos = 0;
-  for (int k = 0; k < n; ++k) {
-    for (int j = k; j < n; ++j, ++pos)
-      if (pos == t) return {k, j, j == n - 1 ? k : -1, (j == n - 1 && k == n - 1) ? k : -1};
-    for (int i = k + 1; i < n; ++i, ++pos)
-      if (pos == t) return {i, k, -1, i == n - 1 ? k : -1};
-  }
-  return {-1, -1, -1, -1};
-}
-// Position of the last MFMA that uses activation (weight) fragment k.
-constexpr int death_a(int k, int n) {
-  for (int t = 0; t < n * n; ++t) if (pass_cell(t, n).end_a == k) return t;
-  return -1;
-}
-constexpr int death_b(int k, int n) {
-  for (int t = 0; t < n * n; ++t) if (pass_cell(t, n).end_b == k) return t;
-  return -1;
-}
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-// LDS reads (two per fragment) that the pass order issues after the MFMAs at
-// positions lo < t < hi.
-constexpr int frag_reads_between(int lo, int hi, int n) {
-  int r = 0;
-  for (int t = lo + 1; t < hi; ++t) {
-    const PassCell c = pass_cell(t, n);
-    r += 2 * ((c.end_a >= 0) + (c.end_b >= 0));
-  }
-  return r;
-}
-template <class F, int... T>
-__device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, T...>) {
-  (f(std::integral_constant<int, T>{}), ...);
-}
-
-// The scaled MFMA as a statement with its accumulator tied (destination = C):
-// written through the builtin, the register allocator moves accumulators
-// between AGPRs around the loop when all 256 hold them, costing copies and
-// hazard waits. It also fixes the MFMA's place in the schedule. The compiler
-// no longer sees the instruction's hazards, so it carries them itself: two
-// wait states ahead of it cover a VALU write of any of its operands just
-// before (the scale exponents, the cleared accumulators); reading results
-// needs mfma_results_ready().
-__device__ __forceinline__ void mfma_scaled(v4f& acc, const v8i& a, const v8i& b, int sa, int sb) {
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
-               : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
-}
-// Wait states between the last MFMAs and any other read of their results (more
-// than the longest XDL write-to-read requirement); the scheduling barrier keeps
-// every later instruction below them.
-__device__ __forceinline__ void mfma_results_ready() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
-
-template <int KIND, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g) {
-  constexpr int WAVES_M = 2, WM = 128, WN = 128, TM = WM / 16, TN = WN / 16, kNT = TM * TN;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave % WAVES_M;
-  const int wave_n = wave / WAVES_M;
-  const int l16 = lane & 15, lq = lane >> 4;
-
-  const Walk wk = make_walk(p);
-  if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
-  const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
-  Loader<KIND, GROUPED, 4, 4> ld(p, g, wk, lds_addr(smem), wave, lane);
-  constexpr int kParts = decltype(ld)::kParts;
-
-  const int sw = swz(l16);
-  const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
-  const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
-  auto a_frag = [&](const uint8_t* stage, int i) { return frag(stage + (wave_m * WM + i * 16) * BK, off0, off1); };
-  auto b_frag = [&](const uint8_t* stage, int j) {
-    return frag(stage + kABytes + (wave_n * WN + j * 16) * BK, off0, off1);
-  };
-  // Exponent bytes of one step: ea[i] of this lane's activation row in subtile
-  // i; eb[j] of its weight row in subtile j (one block scale per wave except
-  // for WGRAD's row scales).
-  // Scales of one step: ra[i] of this lane's activation row in subtile i; rb[j]
-  // of its weight row in subtile j (one block scale per wave except for
-  // WGRAD's row scales). The MFMA takes their exponent bytes.
-  auto read_scales = [&](const uint8_t* stage, float (&ra)[TM], float (&rb)[TN]) {
-    const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
-    const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) ra[i] = Sa[wave_m * WM + i * 16 + l16];
-    if constexpr (KIND == KIND_WGRAD) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) rb[j] = Sb[wave_n * WN + j * 16 + l16];
-    } else {
-      const float v = Sb[wave_n];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) rb[j] = v;
-    }
-  };
-
-#pragma unroll
-  for (int q = 0; q < kParts; ++q) ld.part(q, 0);
-  ld.advance();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kParts; ++q) ld.part(q, 1);
-  ld.advance();
-
-  // A step's fragments all sit in registers before it starts. Its 64 MFMAs
-  // run row 0, column 0, row 1, column 1, ... (each pass over what is left of
-  // that row or column), so activation fragment k is dead after the row-k
-  // pass and weight fragment k after the column-k pass; the next step's copy
-  // of each is read into the same registers right then, which spreads the
-  // step's 16 fragment reads over the step instead of bunching them at its
-  // end. The stage a step was read from is therefore free once the step
-  // begins; the one barrier per step (after the row-0 pass, before the first
-  // read of the next stage) makes it free for every wave and the previous
-  // step's loads visible, and the loads of step s + 2 into stage s % 2 spread
-  // over kSlots MFMAs after it, leaving them the rest of the step to land.
-#ifndef FP8BQ_P2_SLOTS
-#define FP8BQ_P2_SLOTS 40
-#endif
-  constexpr int kFirst = TN;   // the barrier follows the row-0 pass
-  constexpr int kSlots = FP8BQ_P2_SLOTS;
-  static_assert(TM == TN, "the row / column pass order assumes square wave tiles");
-  static_assert(kFirst + kSlots <= kNT, "loads must be issued within the step");
-  // The compiler tracks at most 15 outstanding LDS reads; with more in
-  // flight where a loop iteration begins it waits for all of them before the
-  // first MFMA, which would expose the latency of the step's last reads. An
-  // explicit wait late in each step (for reads issued at least kDrainLag
-  // MFMAs earlier) keeps the count it carries across the loop below that.
-  constexpr int kDrainAt = kNT - 5, kDrainLag = 8;
-  constexpr int kExpReady = kFirst + 12;   // scales are read right after the barrier
-  constexpr int kDrainCnt = frag_reads_between(kDrainAt - kDrainLag, kDrainAt, TM) +
-                            2 * (pass_cell(kDrainAt, TM).end_a >= 0);
-  static_assert(kDrainCnt + frag_reads_between(kDrainAt, kNT, TM) + 2 * (pass_cell(kDrainAt, TM).end_b >= 0) <= 14,
-                "reads in flight at the end of a step must stay countable");
-  v8i af[TM], bf[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) af[i] = a_frag(smem, i);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) bf[j] = b_frag(smem, j);
-  int ea[TM], eb[TN];
-  float ran[TM], rbn[TN];
-  read_scales(smem, ran, rbn);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) ea[i] = e8m0(ran[i]);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) eb[j] = e8m0(rbn[j]);
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the prologue's reads, for the same reason
-
-  v4f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  // wait_loads: the step's barrier also waits for this wave's loads of the
-  // next stage; a tile's first step skips that, its epilogue waited for them
-  // before storing, so the stores stay in flight until the next step.
-  auto step = [&](bool wait_loads) {
-    const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
-    for_each_const([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      constexpr PassCell c = pass_cell(t, TM);
-      mfma_scaled(acc[c.i][c.j], bf[c.j], af[c.i], eb[c.j], ea[c.i]);
-      if constexpr (t >= kFirst && t < kFirst + kSlots) {
-#pragma unroll
-        for (int q = 0; q < kParts; ++q)
-          if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
-      }
-      if constexpr (t + 1 == kNT) ld.advance();
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (c.end_a >= 0) {
-        if constexpr (c.end_a == 0) {
-          if (wait_loads) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          read_scales(nstage, ran, rbn);
-        }
-        af[c.end_a] = a_frag(nstage, c.end_a);
-      }
-      // the next step's exponent of row (column) k replaces this step's once
-      // both its last use has passed and the scale read has had time to land
-      for_each_const([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        if constexpr (cmax(death_a(k, TM), kExpReady) == t) ea[k] = e8m0(ran[k]);
-        if constexpr (cmax(death_b(k, TN), kExpReady) == t) eb[k] = e8m0(rbn[k]);
-      }, std::make_integer_sequence<int, TM>{});
-      if constexpr (t == kDrainAt) __builtin_amdgcn_s_waitcnt(0xC07F | (kDrainCnt << 8));
-      if constexpr (c.end_b >= 0) bf[c.end_b] = b_frag(nstage, c.end_b);
-    }, std::make_integer_sequence<int, kNT>{});
-    ++s;
-  };
-
-#pragma clang loop unroll(disable)
-  for (int tk = 0; tk < my_tiles; ++tk) {
-#pragma clang loop unroll(disable)
-    for (int c = 0; c < nc; ++c) step(c != 0 || tk == 0);
-    mfma_results_ready();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the loads the next tile's first step reads
-
-    // ---- tile done: epilogue --------------------------------------------------
-    const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
-    store_tile<KIND, TM, TN>(p, cur, acc, cur.m0 + wave_m * WM + l16, cur.n0 + wave_n * WN + 4 * lq);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  // the repeated loads after the last step must land before the workgroup's
-  // LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  (void)total;
-}
-
-GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda, const float* sa,
-                   int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                   void* out, int64_t ldo) {
-  GemmArgs p;
-  p.m = m; p.n = n; p.k = k;
-  p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;
-  p.b = b; p.ldb = ldb; p.sb = sb; p.ldsb = ldsb;
-  p.out = out; p.ldo = ldo;
-  p.tiles_m = (int)((m + BM - 1) / BM);
-  p.tiles_n = (int)((n + BN - 1) / BN);
-  return p;
-}
-
-constexpr int kWM = 4;   // 4 x 2 waves of 64 x 128: the accumulator must stay within the
-constexpr int kWN = 2;   // 256 VGPRs the VALU can address, with room for fragments
-#ifndef FP8BQ_LOADERS
-#define FP8BQ_LOADERS 8
-#endif
-constexpr int kLd = FP8BQ_LOADERS;   // waves issuing the operand loads
-constexpr int kBlock = Cfg<kWM, kWN>::kThreads;
-
-// One workgroup per CU (the LDS stages take most of a CU's 160 KB): as many
-// workgroups as CUs, or as tiles when there are fewer tiles.
-int persistent_grid(int tiles) {
-  static int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    return n;
-  }();
-  return tiles < cus ? tiles : cus;
-}
-
-}  // namespace
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
                        const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
@@ -884,31 +25,6 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
     case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
     default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false, kWM, kWN, kLd>), grid, block, 0, st, p, g); break;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, int64_t k,
-                               const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
-                               const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                               uint16_t* out, int64_t ldo, bool pow2, hipStream_t st) {
-  GroupArgs g;
-  g.groups = groups;
-  int tiles = 0;
-  for (int e = 0; e < groups; ++e) {
-    g.tile_prefix[e] = tiles;
-    g.row_off128[e] = (int)(row_off[e] / 128);
-    tiles += (int)((row_off[e + 1] - row_off[e] + BM - 1) / BM);
-  }
-  g.tile_prefix[groups] = tiles;
-  g.row_off128[groups] = (int)(row_off[groups] / 128);
-  GemmArgs p = make_args(row_off[groups], n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
-  p.tiles_m = tiles;
-  if (tiles == 0) return hipSuccess;   // every group empty: nothing to compute
-  const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
-  if (pow2)
-    hipLaunchKernelGGL((gemm_pow2_kernel<KIND_FPROP, true>), grid, dim3(256), 0, st, p, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, true, kWM, kWN, kLd>), grid, block, 0, st, p, g);
   return hipGetLastError();
 }
 

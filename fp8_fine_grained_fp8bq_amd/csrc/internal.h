@@ -29,6 +29,13 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
 // Largest group count the grouped GEMM accepts (offsets travel as kernel arguments).
 constexpr int kMaxGroups = 256;
 
+// The same with a quantised copy of the bf16 output (FPROP / DGRAD only):
+// q [m, n] (ldq) with chunk-major 1x128 scales sq[c * ldsq + row]; out may be
+// null. out_pow2 selects power-of-two output scales.
+hipError_t launch_gemm_quant(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
+                             const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb,
+                             int64_t ldsb, uint16_t* out, int64_t ldo, uint8_t* q, int64_t ldq, float* sq,
+                             int64_t ldsq, bool pow2, bool out_pow2, hipStream_t st);
 hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, int64_t k,
                                const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                                const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,

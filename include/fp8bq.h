@@ -184,6 +184,32 @@ int fp8bq_gemm(int op, int64_t m, int64_t n, int64_t k,
                void* out, int64_t ldo, void* stream);
 
 /*
+ * fp8bq_gemm (FPROP or DGRAD) whose epilogue also quantises the bf16 output as
+ * the activation operand of the next GEMM: producer fusion of the 1x128
+ * quantisation (report section 3.5.2 "online quantization support": without
+ * it the output is written to HBM, read back, quantised, written again and
+ * read once more by the next matrix multiply).
+ *
+ * op, m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb: as fp8bq_gemm; op is
+ *        FP8BQ_FPROP or FP8BQ_DGRAD, optionally | FP8BQ_SCALE_POW2 (input
+ *        scales applied by the matrix instruction).
+ * out    bf16 [m, n] (ldo >= n) as fp8bq_gemm writes it, or NULL when only
+ *        the quantised copy is wanted.
+ * q, s   E4M3 [m, n] (ldq >= n) and chunk-major scales s[c * lds + row]
+ *        (lds >= m): bit for bit what fp8bq_quant_act_1x128 in ROWWISE mode
+ *        (| qflags) writes for the bf16 output.
+ * qflags 0 (s = absmax / 448) or FP8BQ_SCALE_POW2 (power-of-two scales).
+ * Errors: as fp8bq_gemm (out may be NULL); E_INVAL for a WGRAD op, unknown
+ *         qflags, null q or s, ldq < n or lds < m; E_ALIGN unless q is
+ *         16-byte aligned with ldq a multiple of 16 and s 4-byte aligned.
+ */
+int fp8bq_gemm_quant(int op, int64_t m, int64_t n, int64_t k,
+                     const void* a, int64_t lda, const float* sa, int64_t ldsa,
+                     const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                     void* out, int64_t ldo, void* q, int64_t ldq, float* s, int64_t lds,
+                     int qflags, void* stream);
+
+/*
  * Grouped (per-expert) Fprop for the MoE up-projection (report section 3.3.3
  * "low-precision communication": FP8 Fprop of the dispatched activations).
  *

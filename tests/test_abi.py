@@ -35,7 +35,7 @@ def _declared():
 def test_header_declares_the_four_entry_points():
     d = _declared()
     for name in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-                 "fp8bq_grouped_gemm", "fp8bq_last_error"):
+                 "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_last_error"):
         assert name in d
 
 
@@ -136,6 +136,42 @@ def test_gemm_validation(L):
         assert _st(L, f, *bad) == fb.E_INVAL                                   # unknown flag
 
 
+Q16 = 0x50000
+
+
+def _gemm_quant_ok(op=0):
+    # m, n, k = 300, 384, 1024; bf16 output, codes [300, 384] (ldq 384), scales [3, 300]
+    return _gemm_ok(op)[:14] + [Q16, 384, S4, 300, 0, None]
+
+
+def test_gemm_quant_validation(L):
+    f = "fp8bq_gemm_quant"
+    for op in (0, 1):
+        ok = _gemm_quant_ok(op)
+        bad = list(ok); bad[0] = 2
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # WGRAD has no bf16 output
+        bad = list(ok); bad[14] = None
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # null q
+        bad = list(ok); bad[16] = None
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # null s
+        bad = list(ok); bad[18] = 1
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # unknown qflags
+        bad = list(ok); bad[15] = 368
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # ldq < n
+        bad = list(ok); bad[17] = 299
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # lds < m
+        bad = list(ok); bad[14] = Q16 + 4
+        assert _st(L, f, *bad) == fb.E_ALIGN
+        bad = list(ok); bad[15] = 392
+        assert _st(L, f, *bad) == fb.E_ALIGN                                   # ldq % 16
+        bad = list(ok); bad[16] = S4 + 2
+        assert _st(L, f, *bad) == fb.E_ALIGN
+        bad = list(ok); bad[2] = 200; bad[13] = 208; bad[15] = 208
+        assert _st(L, f, *bad) == fb.E_SHAPE                                   # n % 128
+        bad = list(ok); bad[7] = 299
+        assert _st(L, f, *bad) == fb.E_INVAL                                   # ldsa < m
+
+
 def test_grouped_validation(L):
     f = "fp8bq_grouped_gemm"
     P = ctypes.POINTER(ctypes.c_int64)
@@ -188,4 +224,7 @@ def test_valid_arguments_without_device_report_e_device(L):
     assert _st(L, "fp8bq_quant_w_128x128", A16, 256, 384, 384, B16, 384, S4, 3, None, 0, pow2, None) == fb.E_DEVICE
     assert _st(L, "fp8bq_grouped_gemm", 2, off, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56,
                O16, 2048, pow2, None) == fb.E_DEVICE
+    assert _st(L, "fp8bq_gemm_quant", *_gemm_quant_ok(0)) == fb.E_DEVICE
+    no_out = _gemm_quant_ok(1); no_out[12] = None; no_out[18] = pow2
+    assert _st(L, "fp8bq_gemm_quant", *no_out) == fb.E_DEVICE               # bf16 output optional
     assert "device" in L.fp8bq_last_error().decode()
