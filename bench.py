@@ -227,6 +227,52 @@ def main():
     bytes_rq = 2 * M * K + 2 * (M * (K // 128) * 4)
     log(f"[bench] requant 1x128 -> 128x1: {t_rq:.1f} us ({bytes_rq / t_rq / 1e3:.0f} GB/s)")
 
+    # producer fusion: the GEMM quantises its own output (1x128 tiles) for the
+    # next GEMM, against the GEMM followed by the quantiser of its bf16 output
+    yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ysq = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
+
+    def gemm_quant_out():
+        fb.fp8bq_gemm_quant(fb.FPROP, M, N, K, xq.data_ptr(), K, xs.data_ptr(), M, wq.data_ptr(), K,
+                            ws.data_ptr(), K // 128, None, N, yq.data_ptr(), N, ysq.data_ptr(), M, 0, sp)
+
+    def gemm_then_quant():
+        gemm()
+        fb.fp8bq_quant_act_1x128(y.data_ptr(), M, N, N, fb.ACT_ROWWISE, yq.data_ptr(), N, ysq.data_ptr(), M, sp)
+
+    quant_x()
+    quant_w()
+    gemm_quant_out()
+    gemm_then_quant()
+    t_fq, _ = time_kernel(gemm_quant_out, args.kernel_reps, False)
+    t_sq, _ = time_kernel(gemm_then_quant, args.kernel_reps, False)
+    log(f"[bench] GEMM + output quantisation: fused {t_fq:.1f} us, separate {t_sq:.1f} us")
+
+    # decode-shape grouped Fprop (memory-bound): 256 tokens routed top-8, the 8 local
+    # experts' rows unpadded; timed cold (MALL evicted), as weights are in a real decode step
+    dec = workloads.moe_decode()
+    G_d, N_d, K_d = dec.w.shape
+    m_d = int(dec.row_off[-1])
+    d_xq, d_xs = fb.quant_act_1x128(torch.from_numpy(dec.x.view(np.int16)).to(dev))
+    d_wq = torch.empty((G_d, N_d, K_d), dtype=torch.uint8, device=dev)
+    d_ws = torch.empty((G_d, N_d // 128, K_d // 128), dtype=torch.float32, device=dev)
+    for e in range(G_d):
+        q_e, s_e, _ = fb.quant_w_128x128(torch.from_numpy(dec.w[e].view(np.int16)).to(dev))
+        d_wq[e].copy_(q_e)
+        d_ws[e].copy_(s_e)
+    d_y = torch.empty((m_d, N_d), dtype=torch.bfloat16, device=dev)
+    d_off = [int(v) for v in dec.row_off]
+
+    def decode():
+        fb.fp8bq_grouped_gemm_decode(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
+                                     d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d, 0, sp)
+
+    decode()
+    t_dec, _ = time_kernel(decode, args.kernel_reps, True)
+    bytes_dec = (G_d * N_d * K_d + G_d * (N_d // 128) * (K_d // 128) * 4 + m_d * K_d + m_d * (K_d // 128) * 4
+                 + m_d * N_d * 2)
+    log(f"[bench] decode grouped Fprop ({m_d} rows): {t_dec:.1f} us ({bytes_dec / t_dec / 1e3:.0f} GB/s)")
+
     tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
     tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
     tg, tg_med = time_kernel(gemm, args.kernel_reps, False)
@@ -291,6 +337,25 @@ def main():
                 "ms_per_step": round(ms_step_p2, 4), "gemm_us": round(tg_p2, 2),
                 "gemm_TFLOPs": round(flops / (tg_p2 * 1e-6) / 1e12, 1),
                 "kernel": "gemm_pow2_kernel<FPROP>",
+            },
+            "producer_fusion": {
+                "what": "GEMM whose epilogue writes Y as E4M3 codes + 1x128 scales (no bf16 Y), against the GEMM "
+                        "writing bf16 Y followed by the 1x128 quantiser of Y",
+                "fused_us": round(t_fq, 2), "separate_us": round(t_sq, 2),
+                "fused_TFLOPs": round(flops / (t_fq * 1e-6) / 1e12, 1),
+                "hbm_bytes_saved": 4 * M * N,
+                "kernel": "gemm_kernel<FPROP, QMODE=1>",
+            },
+            "decode_grouped": {
+                "what": f"{dec.name}: rows per expert {[int(c) for c in dec.real_rows]} (unpadded), "
+                        "bf16 out; HBM-bound (each expert's FP8 weight streamed once); timed cold",
+                "us": round(t_dec, 2), "GBps": round(bytes_dec / t_dec / 1e3, 1),
+                "roofline": {"bound": "hbm", "achieved": round(bytes_dec / t_dec / 1e3, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(bytes_dec / t_dec / 1e3 / PEAK_HBM_GBS, 4),
+                             "traffic": None},
+                "algorithmic_bytes": bytes_dec,
+                "TFLOPs": round(2.0 * m_d * N_d * K_d / (t_dec * 1e-6) / 1e12, 1),
+                "kernel": "gemm_decode_kernel",
             },
         },
     }

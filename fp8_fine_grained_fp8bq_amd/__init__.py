@@ -9,13 +9,13 @@ fallback: if the library is missing or the device is not gfx950, calls raise.
 Two layers with the C names:
 
 * `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
-  `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`: pointer-level,
-  exactly the C signatures (ints for pointers and the stream); a non-zero
-  status raises `Fp8bqError`.
+  `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`,
+  `fp8bq_grouped_gemm_decode`: pointer-level, exactly the C signatures (ints
+  for pointers and the stream); a non-zero status raises `Fp8bqError`.
 * `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
-  `gemm_quant`, `grouped_gemm`: take torch tensors on the GPU, allocate the
-  outputs with torch (memory and streams are the only things torch provides)
-  and call the same entry points on the current stream.
+  `gemm_quant`, `grouped_gemm`, `grouped_gemm_decode`: take torch tensors on
+  the GPU, allocate the outputs with torch (memory and streams are the only
+  things torch provides) and call the same entry points on the current stream.
 """
 
 from __future__ import annotations
@@ -33,7 +33,8 @@ ACT_ROWWISE, ACT_COLWISE = 0, 1
 SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_last_error", "fp8bq_version")
+           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_last_error",
+           "fp8bq_version")
 
 
 class Fp8bqError(RuntimeError):
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
                   "fp8bq_grouped_gemm"):
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
+        L.fp8bq_grouped_gemm_decode.argtypes = L.fp8bq_grouped_gemm.argtypes
         L.fp8bq_last_error.argtypes = []
         L.fp8bq_version.restype = ctypes.c_char_p
         L.fp8bq_version.argtypes = []
@@ -117,6 +119,15 @@ def fp8bq_grouped_gemm(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb
     return _check("fp8bq_grouped_gemm",
                   lib().fp8bq_grouped_gemm(groups, arr, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb,
                                            out, ldo, flags, stream))
+
+
+def fp8bq_grouped_gemm_decode(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, flags=0,
+                              stream=0):
+    """`row_off` is a sequence of groups + 1 ints (host memory), any counts up to 256 per group."""
+    arr = (ctypes.c_int64 * (groups + 1))(*[int(v) for v in row_off]) if row_off is not None else None
+    return _check("fp8bq_grouped_gemm_decode",
+                  lib().fp8bq_grouped_gemm_decode(groups, arr, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb,
+                                                  out, ldo, flags, stream))
 
 
 def version() -> str:
@@ -235,4 +246,19 @@ def grouped_gemm(row_off, a, sa, b, sb, out=None, pow2: bool = False):
     fp8bq_grouped_gemm(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
                        b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
                        out.stride(0), SCALE_POW2 if pow2 else 0, _stream(a))
+    return out
+
+
+def grouped_gemm_decode(row_off, a, sa, b, sb, out=None):
+    """Decode-shape grouped Fprop: row_off host sequence of G + 1 offsets (any counts up to
+    256 rows per expert); a uint8 [m, k]; sa [k/128, >=m]; b uint8 [G, n, k];
+    sb float32 [G, n/128, k/128]. Returns bf16 [m, n]."""
+    import torch
+    G, n, k = b.shape
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    fp8bq_grouped_gemm_decode(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
+                              b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
+                              out.stride(0), 0, _stream(a))
     return out

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8bq.so")
 
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "gemm_quant.hip", "gemm_grouped.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "gemm_quant.hip", "gemm_grouped.hip", "gemm_decode.hip"]
 
 # -packed-fp32-ops: no packed FP32 VALU instructions (v_pk_*_f32) in any kernel.
 # -Wno-inline-asm: the LDS-DMA helpers name M0 (a compiler-reserved register) as

@@ -239,4 +239,34 @@ int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_
                   "grouped_gemm");
 }
 
+int fp8bq_grouped_gemm_decode(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
+                              int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
+                              const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags, void* stream) {
+  if (flags != 0) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: flags must be 0, got %d", flags);
+  if (groups < 1 || groups > fp8bq::kMaxGroups)
+    return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: groups must be in [1, %d], got %d", fp8bq::kMaxGroups, groups);
+  if (!row_off) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: null row_off");
+  if (row_off[0] != 0) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: row_off[0] must be 0");
+  for (int e = 0; e < groups; ++e) {
+    const int64_t rows = row_off[e + 1] - row_off[e];
+    if (rows < 0) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: row_off must be non-decreasing (at %d)", e);
+    if (rows > fp8bq::kMaxDecodeRows)
+      return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: group %d has %lld rows, at most %d", e, (long long)rows,
+                  fp8bq::kMaxDecodeRows);
+  }
+  const int64_t m = row_off[groups];
+  if (int st = check_gemm_common("grouped_gemm_decode", m > 0 ? m : 1, n, k, a, lda, sa, b, ldb, sb, out, ldo, 2))
+    return st;
+  if ((int64_t)groups * (n / 64) >= ((int64_t)1 << 31)) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: too many column slices");
+  if (ldsa < m) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsa must be >= m");
+  if (ldsb < k / 128) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsb must be >= k / 128");
+  if (int st = check_device()) return st;
+  if (m == 0) return FP8BQ_OK;
+  return launched(fp8bq::launch_grouped_gemm_decode(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda, sa,
+                                                    ldsa, static_cast<const uint8_t*>(b), ldb, sb, ldsb,
+                                                    static_cast<uint16_t*>(out), ldo,
+                                                    reinterpret_cast<hipStream_t>(stream)),
+                  "grouped_gemm_decode");
+}
+
 }  // extern "C"

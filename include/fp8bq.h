@@ -232,6 +232,25 @@ int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_
                        const void* b, int64_t ldb, const float* sb, int64_t ldsb,
                        void* out, int64_t ldo, int flags, void* stream);
 
+/*
+ * Grouped Fprop for decode-sized expert batches (report section 3.4.2
+ * "decoding stage": each expert then sees a small batch, at most about 256
+ * tokens, and the step is bound by memory access, chiefly the experts' FP8
+ * weights). Same operation, operands and scales as fp8bq_grouped_gemm, but the
+ * experts' rows are not padded: row_off may hold any non-decreasing offsets
+ * with row_off[0] == 0 and at most 256 rows per expert (an expert may be
+ * empty). The kernel streams each expert's weight once; it is the memory-bound
+ * counterpart of fp8bq_grouped_gemm.
+ *
+ * flags  must be 0 (scales are applied as floats by the FP32 promotion, which
+ *        power-of-two scales satisfy too).
+ * Errors: as fp8bq_grouped_gemm; E_SHAPE for a group of more than 256 rows.
+ */
+int fp8bq_grouped_gemm_decode(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                              const void* a, int64_t lda, const float* sa, int64_t ldsa,
+                              const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                              void* out, int64_t ldo, int flags, void* stream);
+
 /* Thread-local description of the last non-OK status on this thread. */
 const char* fp8bq_last_error(void);
 

@@ -35,7 +35,7 @@ def _declared():
 def test_header_declares_the_four_entry_points():
     d = _declared()
     for name in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-                 "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_last_error"):
+                 "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_last_error"):
         assert name in d
 
 
@@ -194,6 +194,27 @@ def test_grouped_validation(L):
     assert isinstance(P, type)
 
 
+def test_grouped_decode_validation(L):
+    f = "fp8bq_grouped_gemm_decode"
+
+    def off(*v):
+        return (ctypes.c_int64 * len(v))(*v)
+    base = [None, 2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56, O16, 2048, 0, None]
+    assert _st(L, f, 0, off(0), *base[1:]) == fb.E_INVAL
+    assert _st(L, f, 2, None, *base[1:]) == fb.E_INVAL
+    assert _st(L, f, 2, off(3, 10, 20), *base[1:]) == fb.E_SHAPE              # row_off[0] != 0
+    assert _st(L, f, 2, off(0, 30, 20), *base[1:]) == fb.E_SHAPE              # decreasing
+    assert _st(L, f, 2, off(0, 257, 300), *base[1:]) == fb.E_SHAPE            # a group of 257 rows
+    bad = list(base); bad[13] = 1
+    assert _st(L, f, 2, off(0, 30, 50), *bad[1:]) == fb.E_INVAL               # flags
+    bad = list(base); bad[6] = 40
+    assert _st(L, f, 2, off(0, 30, 50), *bad[1:]) == fb.E_INVAL               # ldsa < m
+    bad = list(base); bad[1] = 2000; bad[12] = 2000
+    assert _st(L, f, 2, off(0, 30, 50), *bad[1:]) == fb.E_SHAPE              # n % 128
+    bad = list(base); bad[3] = A16 + 8
+    assert _st(L, f, 2, off(0, 30, 50), *bad[1:]) == fb.E_ALIGN
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(fb.Fp8bqError) as ei:
         fb.fp8bq_gemm(7, 1, 128, 128, A16, 128, S4, 1, B16, 128, S4, 1, O16, 128, 0)
@@ -227,4 +248,6 @@ def test_valid_arguments_without_device_report_e_device(L):
     assert _st(L, "fp8bq_gemm_quant", *_gemm_quant_ok(0)) == fb.E_DEVICE
     no_out = _gemm_quant_ok(1); no_out[12] = None; no_out[18] = pow2
     assert _st(L, "fp8bq_gemm_quant", *no_out) == fb.E_DEVICE               # bf16 output optional
+    assert _st(L, "fp8bq_grouped_gemm_decode", 3, (ctypes.c_int64 * 4)(0, 17, 17, 273), 2048, 7168, A16, 7168,
+               S4, 512, B16, 7168, S4, 56, O16, 2048, 0, None) == fb.E_DEVICE
     assert "device" in L.fp8bq_last_error().decode()

@@ -137,6 +137,18 @@ def moe_fprop(seed: int = 1004, tokens: int = 16384, n: int = 2048, k: int = 716
                x, w, row_off, counts)
 
 
+def moe_decode(seed: int = 1006, tokens: int = 256, n: int = 2048, k: int = 7168, local: int = 8) -> MoE:
+    """Decode step of the MoE up-projection: `tokens` tokens routed top-8 over 256 experts
+    (Zipf 1.1), the `local` most popular experts' rows stacked without padding (each at
+    most `tokens` rows), X ~ N(0, 1), W_e ~ N(0, 0.02)."""
+    rr, rx, rw = np.random.default_rng(seed).spawn(3)
+    counts = moe_routing_counts(int(rr.integers(0, 2**31)), tokens=tokens, local=local)
+    row_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    x = f32_to_bf16_bits(_normal(rx, (int(row_off[-1]), k)))
+    w = np.stack([f32_to_bf16_bits(_normal(rw, (n, k), 0.02)) for _ in range(local)])
+    return MoE(f"MoE decode {local} experts, {tokens} tokens top-8, N={n} K={k}", x, w, row_off, counts)
+
+
 # E4M3 byte patterns of 0, +-0.5, +-1, +-1.5, +-2, +-3, +-4. A product of two of
 # these is a multiple of 1/4 below 16 in magnitude, so a block-scaled GEMM over
 # such codes with power-of-two scales near 1 is exact in fp32 (every partial
