@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="large")
     ap.add_argument("--kernel-reps", type=int, default=10, help="reps of each kernel timed alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the dense, backward and MoE configurations' kernels")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample: rows of X")
     ap.add_argument("--cpu-wrows", type=int, default=8192, help="oracle sample: rows of W")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -273,6 +275,96 @@ def main():
                  + m_d * N_d * 2)
     log(f"[bench] decode grouped Fprop ({m_d} rows): {t_dec:.1f} us ({bytes_dec / t_dec / 1e3:.0f} GB/s)")
 
+    # the other configurations' kernels, each timed alone (GEMMs warm, quantisers cold):
+    # dense fprop, the backward pair (Dgrad, Wgrad with token-direction 128x1
+    # quantisation) and the MoE grouped fprop
+    others = {}
+    if not args.no_other_configs:
+        t0 = time.perf_counter()
+        dn = workloads.dense_fprop()
+        dyb = workloads.backward_dy()
+        moe = workloads.moe_fprop()
+        log(f"[bench] generated the other configurations in {time.perf_counter() - t0:.1f}s")
+        o_x = torch.from_numpy(dn.x.view(np.int16)).to(dev)
+        o_w = torch.from_numpy(dn.w.view(np.int16)).to(dev)
+        o_dy = torch.from_numpy(dyb.view(np.int16)).to(dev)
+        Md, Nd, Kd = dn.x.shape[0], dn.w.shape[0], dn.x.shape[1]
+        o_xq, o_xs = fb.quant_act_1x128(o_x)
+        o_wq, o_ws, o_wqt = fb.quant_w_128x128(o_w, transposed_copy=True)
+        o_y = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+        o_dq, o_ds = fb.quant_act_1x128(o_dy)
+        o_dx = torch.empty((Md, Kd), dtype=torch.bfloat16, device=dev)
+        o_dqt = torch.empty((Nd, Md), dtype=torch.uint8, device=dev)
+        o_dst = torch.empty((Md // 128, Nd), dtype=torch.float32, device=dev)
+        o_xqt = torch.empty((Kd, Md), dtype=torch.uint8, device=dev)
+        o_xst = torch.empty((Md // 128, Kd), dtype=torch.float32, device=dev)
+        o_dw = torch.empty((Nd, Kd), dtype=torch.float32, device=dev)
+
+        def o_fprop():
+            fb.fp8bq_gemm(fb.FPROP, Md, Nd, Kd, o_xq.data_ptr(), Kd, o_xs.data_ptr(), Md, o_wq.data_ptr(), Kd,
+                          o_ws.data_ptr(), Kd // 128, o_y.data_ptr(), Nd, sp)
+
+        def o_dgrad():
+            fb.fp8bq_gemm(fb.DGRAD, Md, Kd, Nd, o_dq.data_ptr(), Nd, o_ds.data_ptr(), Md, o_wqt.data_ptr(), Nd,
+                          o_ws.data_ptr(), Kd // 128, o_dx.data_ptr(), Kd, sp)
+
+        def o_qcol_dy():
+            fb.fp8bq_quant_act_1x128(o_dy.data_ptr(), Md, Nd, Nd, fb.ACT_COLWISE, o_dqt.data_ptr(), Md,
+                                     o_dst.data_ptr(), Nd, sp)
+
+        def o_qcol_x():
+            fb.fp8bq_quant_act_1x128(o_x.data_ptr(), Md, Kd, Kd, fb.ACT_COLWISE, o_xqt.data_ptr(), Md,
+                                     o_xst.data_ptr(), Kd, sp)
+
+        def o_wgrad():
+            fb.fp8bq_gemm(fb.WGRAD, Nd, Kd, Md, o_dqt.data_ptr(), Md, o_dst.data_ptr(), Nd, o_xqt.data_ptr(), Md,
+                          o_xst.data_ptr(), Kd, o_dw.data_ptr(), Kd, sp)
+
+        for fn in (o_fprop, o_dgrad, o_qcol_dy, o_qcol_x, o_wgrad):
+            fn()
+        t_of, _ = time_kernel(o_fprop, args.kernel_reps, False)
+        t_od, _ = time_kernel(o_dgrad, args.kernel_reps, False)
+        t_ow, _ = time_kernel(o_wgrad, args.kernel_reps, False)
+        t_qc, _ = time_kernel(o_qcol_x, args.kernel_reps, True)
+        f_d = 2.0 * Md * Nd * Kd
+        b_qc = Md * Kd * 3 + (Md // 128) * Kd * 4
+        others["dense_fprop"] = {"what": f"GEMM {Md}x{Nd}x{Kd} (bf16 out)", "us": round(t_of, 2),
+                                 "TFLOPs": round(f_d / (t_of * 1e-6) / 1e12, 1)}
+        others["dgrad"] = {"what": f"dX = dY W: GEMM {Md}x{Kd}x{Nd} (bf16 out)", "us": round(t_od, 2),
+                           "TFLOPs": round(f_d / (t_od * 1e-6) / 1e12, 1)}
+        others["wgrad"] = {"what": f"dW = dY^T X: GEMM {Nd}x{Kd}x{Md} over tokens, 128x1-quantised operands (fp32 out)",
+                           "us": round(t_ow, 2), "TFLOPs": round(f_d / (t_ow * 1e-6) / 1e12, 1)}
+        others["quant_act_128x1"] = {"what": f"token-direction (128x1) quantisation of X [{Md}, {Kd}], transposed out",
+                                     "us": round(t_qc, 2), "GBps": round(b_qc / t_qc / 1e3, 1),
+                                     "frac_hbm": round(b_qc / t_qc / 1e3 / PEAK_HBM_GBS, 4)}
+        del o_x, o_w, o_dy, o_y, o_dx, o_dw
+        # MoE grouped fprop (8 local experts, Zipf top-8 routing, rows padded to 128)
+        G_m, N_m, K_m = moe.w.shape
+        m_m = int(moe.row_off[-1])
+        g_xq, g_xs = fb.quant_act_1x128(torch.from_numpy(moe.x.view(np.int16)).to(dev))
+        g_wq = torch.empty((G_m, N_m, K_m), dtype=torch.uint8, device=dev)
+        g_ws = torch.empty((G_m, N_m // 128, K_m // 128), dtype=torch.float32, device=dev)
+        for e in range(G_m):
+            q_e, s_e, _ = fb.quant_w_128x128(torch.from_numpy(moe.w[e].view(np.int16)).to(dev))
+            g_wq[e].copy_(q_e)
+            g_ws[e].copy_(s_e)
+        g_y = torch.empty((m_m, N_m), dtype=torch.bfloat16, device=dev)
+        g_off = [int(v) for v in moe.row_off]
+
+        def o_grouped():
+            fb.fp8bq_grouped_gemm(G_m, g_off, N_m, K_m, g_xq.data_ptr(), K_m, g_xs.data_ptr(), m_m, g_wq.data_ptr(),
+                                  K_m, g_ws.data_ptr(), K_m // 128, g_y.data_ptr(), N_m, 0, sp)
+
+        o_grouped()
+        t_og, _ = time_kernel(o_grouped, args.kernel_reps, False)
+        f_real = 2.0 * float(np.sum(moe.real_rows)) * N_m * K_m
+        others["moe_grouped"] = {"what": f"{moe.name}: {m_m} rows padded to 128 per expert "
+                                         f"({int(np.sum(moe.real_rows))} routed)",
+                                 "us": round(t_og, 2), "TFLOPs_routed_rows": round(f_real / (t_og * 1e-6) / 1e12, 1),
+                                 "TFLOPs_padded_rows": round(2.0 * m_m * N_m * K_m / (t_og * 1e-6) / 1e12, 1)}
+        log(f"[bench] other configs: dense {t_of:.1f} us, dgrad {t_od:.1f} us, wgrad {t_ow:.1f} us, "
+            f"128x1 quant {t_qc:.1f} us, MoE grouped {t_og:.1f} us")
+
     tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
     tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
     tg, tg_med = time_kernel(gemm, args.kernel_reps, False)
@@ -330,6 +422,7 @@ def main():
             "requant_t_frac_hbm": round(bytes_rq / t_rq / 1e3 / PEAK_HBM_GBS, 4),
             "quant_timing": "each kernel alone after a 512 MB read (MALL evicted), HIP events, mean",
         },
+        "other_configs": others,
         "variants": {
             "pow2_scales": {
                 "what": "the same step with power-of-two scales, applied by the scaled matrix instruction",
