@@ -21,7 +21,8 @@
 //  * The weight tile is the MFMA's first operand and the activation tile its
 //    second, so a lane's four result registers are four consecutive output
 //    columns j of one output row i: one activation scale per (lane, 16-row
-//    subtile) per chunk and 8-byte (bf16) / 16-byte (fp32) output stores.
+//    subtile) per chunk; the epilogue regroups pairs of lanes so that every
+//    lane stores 16 bytes (bf16 and fp32 alike).
 //  * Workgroup tile 256 x 256, 8 waves (two per SIMD) of 64 x 128: 128
 //    accumulator VGPRs per lane (the promotion FMAs need the accumulator in the
 //    256 VGPRs the VALU can address, which rules out 128 x 128 wave tiles),
@@ -244,11 +245,62 @@ __device__ __forceinline__ Walk make_walk(const GemmArgs& p) {
 }
 
 // ---- epilogue ----------------------------------------------------------------
+// bf16 pair of four accumulators (round to nearest even: hardware
+// v_cvt_pk_bf16_f32, equal to the integer rounding on every finite fp32).
+__device__ __forceinline__ uint2 pack_bf16x4(const v4f& v) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+  uint2 r;
+  __builtin_memcpy(&r.x, &lo, 4);
+  __builtin_memcpy(&r.y, &hi, 4);
+  return r;
+}
+
+// Two subtiles' bf16 results (A of subtile j, B of subtile j + 1; lane: row
+// l16, columns 4 lq .. 4 lq + 3) regrouped between lanes lq and lq ^ 1 into
+// 16 contiguous bytes per lane: even lanes take columns 4 lq .. 4 lq + 7 of
+// subtile j, odd lanes columns 4 lq - 4 .. 4 lq + 3 of subtile j + 1. Stores
+// cost per active lane, so 16-byte lanes halve the epilogue's store work.
+// Returns the 16 bytes; they go to the lane's own column of subtile j (even
+// lanes) or 12 columns on from it (odd lanes).
+__device__ __forceinline__ uint4 pair16(uint2 A, uint2 B, bool odd) {
+  const uint2 snd = odd ? A : B;
+  uint2 rcv;
+  rcv.x = (uint32_t)__shfl_xor((int)snd.x, 16);
+  rcv.y = (uint32_t)__shfl_xor((int)snd.y, 16);
+  return odd ? make_uint4(rcv.x, rcv.y, B.x, B.y) : make_uint4(A.x, A.y, rcv.x, rcv.y);
+}
+
+// The codes of four subtiles of one output row (d[k]: columns 16 k + 4 lq ..
+// 16 k + 4 lq + 3 of subtile group g, from lane lq of the row) transposed
+// between the row's four lanes (two exchange rounds, partners lq ^ 1 and
+// lq ^ 2): lane lq ends with the 16 codes of subtile 4 g + lq, one 16-byte
+// store instead of four 4-byte ones.
+__device__ __forceinline__ uint4 codes16(const uint32_t (&d)[4], int lq) {
+  const bool b0 = (lq & 1) != 0, b1 = (lq & 2) != 0;
+  // round 1: keep the dwords whose index has bit 0 = b0, swap the others
+  const uint32_t s0 = b0 ? d[0] : d[1], s1 = b0 ? d[2] : d[3];
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 16), r1 = (uint32_t)__shfl_xor((int)s1, 16);
+  const uint32_t own_lo = b0 ? d[1] : d[0], own_hi = b0 ? d[3] : d[2];
+  // now: own_lo / own_hi = this lane's index b0 / b0 + 2, r0 / r1 the partner's
+  // round 2: keep index lq (= b0 + 2 b1), swap index lq ^ 2
+  const uint32_t x_keep = b1 ? own_hi : own_lo, y_keep = b1 ? r1 : r0;
+  const uint32_t x_send = b1 ? own_lo : own_hi, y_send = b1 ? r0 : r1;
+  const uint32_t rx = (uint32_t)__shfl_xor((int)x_send, 32), ry = (uint32_t)__shfl_xor((int)y_send, 32);
+  // source lanes: lq (x_keep), lq ^ 1 (y_keep), lq ^ 2 (rx), lq ^ 3 (ry)
+  uint32_t o[4];
+#pragma unroll
+  for (int src = 0; src < 4; ++src) {
+    const int rel = src ^ lq;
+    o[src] = rel == 0 ? x_keep : rel == 1 ? y_keep : rel == 2 ? rx : ry;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Stores a wave's TM x TN subtiles (lane: output row l16 of subtile i, columns
-// 4 lq .. 4 lq + 3 of subtile j) as bf16 (round to nearest even, hardware
-// v_cvt_pk_bf16_f32, equal to the integer rounding on every finite fp32) or
-// fp32. Full tiles take one row pointer per subtile row and constant column
-// offsets; edge tiles check every row and column.
+// 4 lq .. 4 lq + 3 of subtile j) as bf16 or fp32. Full bf16 tiles store 16
+// bytes per lane (pair16) with one row pointer per subtile row; edge tiles
+// check every row and column.
 template <int KIND, int TM, int TN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
                                            int64_t row0, int64_t col0) {
@@ -256,19 +308,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
     if constexpr (KIND == KIND_WGRAD) {
       *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + row * p.ldo + col) = v;
     } else {
-      const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-      const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-      uint2 packed;
-      __builtin_memcpy(&packed.x, &lo, 4);
-      __builtin_memcpy(&packed.y, &hi, 4);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col) = packed;
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col) = pack_bf16x4(v);
     }
   };
   if (cur.m_end - cur.m0 == BM && cur.n_end - cur.n0 == BN) {   // uniform
+    if constexpr (KIND == KIND_WGRAD) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
+        for (int j = 0; j < TN; ++j) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
+    } else {
+      const bool odd = ((threadIdx.x >> 4) & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < TN / 2; ++jp) {
+          const uint4 v = pair16(pack_bf16x4(acc[i][2 * jp]), pack_bf16x4(acc[i][2 * jp + 1]), odd);
+          const int64_t col = col0 + 2 * jp * 16 + (odd ? 12 : 0);
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (row0 + i * 16) * p.ldo + col) = v;
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -286,8 +345,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
 // (32 values each): each lane takes the max of its bf16 magnitudes, two lane
 // exchanges give the tile's, and scale and codes come from the quantisers'
 // codec (fp8_codec.h) applied to the same bf16 values, so q / sq equal
-// fp8bq_quant_act_1x128 of the bf16 output bit for bit. The bf16 output itself
-// is written only when p.out is set. grp is the tile's 128-column group.
+// fp8bq_quant_act_1x128 of the bf16 output bit for bit. The codes are
+// transposed among the row's lanes (codes16) into 16-byte stores. The bf16
+// output itself is written only when p.out is set. grp is the tile's
+// 128-column group.
 template <bool POW2, int TM, int TN>
 __device__ __forceinline__ void store_tile_q(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
                                              int64_t row0, int64_t col0, int64_t grp, int lq) {
@@ -310,12 +371,31 @@ __device__ __forceinline__ void store_tile_q(const GemmArgs& p, const Tile& cur,
     amax = umax(amax, (uint32_t)__shfl_xor((int)amax, 16));
     amax = umax(amax, (uint32_t)__shfl_xor((int)amax, 32));
     const TileScale ts = group_scale<POW2>(amax);
-    if (row < cur.m_end) {
+    uint32_t code[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint32_t code = encode4<POW2>(bf_lo(w[j].x), bf_hi(w[j].x), bf_lo(w[j].y), bf_hi(w[j].y), ts);
-        *reinterpret_cast<uint32_t*>(p.q + row * p.ldq + col0 + j * 16) = code;
-        if (bf_out) *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col0 + j * 16) = w[j];
+    for (int j = 0; j < TN; ++j)
+      code[j] = encode4<POW2>(bf_lo(w[j].x), bf_hi(w[j].x), bf_lo(w[j].y), bf_hi(w[j].y), ts);
+    // lane exchanges (every lane of the wave takes part) before the row check
+    uint4 c16[TN / 4], b16[TN / 2];
+#pragma unroll
+    for (int g = 0; g < TN / 4; ++g) {
+      const uint32_t d[4] = {code[4 * g], code[4 * g + 1], code[4 * g + 2], code[4 * g + 3]};
+      c16[g] = codes16(d, lq);
+    }
+    if (bf_out) {
+#pragma unroll
+      for (int jp = 0; jp < TN / 2; ++jp) b16[jp] = pair16(w[2 * jp], w[2 * jp + 1], (lq & 1) != 0);
+    }
+    if (row < cur.m_end) {
+      const int64_t gcol = col0 - 4 * lq;       // the wave's first column
+#pragma unroll
+      for (int g = 0; g < TN / 4; ++g)
+        *reinterpret_cast<uint4*>(p.q + row * p.ldq + gcol + 16 * (4 * g + lq)) = c16[g];
+      if (bf_out) {
+#pragma unroll
+        for (int jp = 0; jp < TN / 2; ++jp)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col0 + 2 * jp * 16 +
+                                    ((lq & 1) ? 12 : 0)) = b16[jp];
       }
       if (lq == 0) p.sq[grp * p.ldsq + row] = ts.s;
     }
