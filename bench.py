@@ -174,12 +174,16 @@ def main():
 
     # bring the GPU to its sustained-load clock first: a kernel timed after idling
     # runs up to ~15% slower than the same kernel after ~50 ms of back-to-back work
-    s0, settle_steps = time.perf_counter(), 0
-    while (time.perf_counter() - s0) * 1e3 < args.settle_ms:
-        for _ in range(10):
-            step()
-        settle_steps += 10
-        torch.cuda.synchronize()
+    def settle(ms):
+        s0, n = time.perf_counter(), 0
+        while (time.perf_counter() - s0) * 1e3 < ms:
+            for _ in range(5):
+                step()
+            n += 5
+            torch.cuda.synchronize()
+        return n
+
+    settle_steps = settle(args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -200,8 +204,10 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), {value:.1f} TFLOP/s")
 
     # each kernel alone; the quantisers after a 512 MB read that evicts the MALL
-    # reps are queued back to back (no host wait between them, so the GPU does not idle)
+    # reps are queued back to back (no host wait between them, so the GPU does not
+    # idle), after steps that bring the clock back up from any idle time before
     def time_kernel(fn, reps, cold):
+        settle(min(150.0, args.settle_ms))
         evs = []
         for _ in range(reps):
             if cold:
