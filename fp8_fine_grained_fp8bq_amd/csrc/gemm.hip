@@ -1,15 +1,32 @@
 // Launcher of the block-scaled FP8 GEMM (fp8bq_gemm): the VALU-promotion
-// kernel for general scales, the scaled-MFMA kernel for power-of-two scales.
+// kernel for general scales (256 x 256 tiles, or 256 x 128 when there are too
+// few of those to fill the CUs), the scaled-MFMA kernel for power-of-two scales.
 #include "gemm_kernels.h"
 
 namespace fp8bq {
 
+// GEMMs with at most this many 256 x 256 tiles (half the CUs or fewer) run
+// with 256 x 128 tiles instead: twice the workgroups, each with half the work.
+constexpr int64_t kNarrowTiles = 128;
+
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
                        const float* sa, int64_t ldsa, const uint8_t* b, int64_t ldb,
                        const float* sb, int64_t ldsb, void* out, int64_t ldo, bool pow2, hipStream_t st) {
-  GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   GroupArgs g;
   g.groups = 0;
+  const int64_t tiles256 = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if (!pow2 && tiles256 <= kNarrowTiles) {
+    constexpr int kNarrow = 128;
+    GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, kNarrow);
+    const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
+    switch (kind) {
+      case KIND_FPROP: hipLaunchKernelGGL((gemm_kernel<KIND_FPROP, false, kWM, kWN, kLd, 0, kNarrow>), grid, block, 0, st, p, g); break;
+      case KIND_DGRAD: hipLaunchKernelGGL((gemm_kernel<KIND_DGRAD, false, kWM, kWN, kLd, 0, kNarrow>), grid, block, 0, st, p, g); break;
+      default:         hipLaunchKernelGGL((gemm_kernel<KIND_WGRAD, false, kWM, kWN, kLd, 0, kNarrow>), grid, block, 0, st, p, g); break;
+    }
+    return hipGetLastError();
+  }
+  GemmArgs p = make_args(m, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo);
   const dim3 grid((unsigned)persistent_grid(p.tiles_m * p.tiles_n)), block(kBlock);
   if (pow2) {
     const dim3 block4(256);

@@ -53,25 +53,36 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Workgroup tile: BM rows x TBN columns, TBN = 256 (BN) or, for GEMMs with
+// too few 256 x 256 tiles to fill the CUs, 128.
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kABytes = BM * BK;
-constexpr int kBBytes = BN * BK;
-constexpr int kSaOff = kABytes + kBBytes;
-constexpr int kSbOff = kSaOff + BM * 4;
-constexpr int kStage = kSbOff + BN * 4;
+// One LDS stage: the A and B tiles of a K-chunk, BM activation scales, and
+// room for 256 weight-side scales (column scales of WGRAD, else the tile's
+// weight block scales).
+template <int TBN>
+struct Stage {
+  static constexpr int kABytes = BM * BK;
+  static constexpr int kBBytes = TBN * BK;
+  static constexpr int kSaOff = kABytes + kBBytes;
+  static constexpr int kSbOff = kSaOff + BM * 4;
+  static constexpr int kStage = kSbOff + 256 * 4;
+};
+constexpr int kABytes = Stage<BN>::kABytes;
+constexpr int kSaOff = Stage<BN>::kSaOff;
+constexpr int kSbOff = Stage<BN>::kSbOff;
+constexpr int kStage = Stage<BN>::kStage;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
-template <int WAVES_M, int WAVES_N>
+template <int WAVES_M, int WAVES_N, int TBN = BN>
 struct Cfg {
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M;
-  static constexpr int WN = BN / WAVES_N;
+  static constexpr int WN = TBN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
-  static_assert(WN == 128, "one weight block column per wave");
-  static_assert(BM == BN, "square workgroup tile");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one weight block column");
 };
 
 struct GemmArgs {
@@ -184,7 +195,7 @@ struct Tile {
   const float* sb;
 };
 
-template <bool GROUPED>
+template <bool GROUPED, int TBN = BN>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g, int logical) {
   const int per_group = kGroupM * p.tiles_n;
   const int group = logical / per_group;
@@ -215,8 +226,8 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g,
     t.m0 = (int64_t)tmi * BM;
     t.m_end = min(t.m0 + BM, p.m);
   }
-  t.n0 = (int64_t)tni * BN;
-  t.n_end = min(t.n0 + BN, p.n);
+  t.n0 = (int64_t)tni * TBN;
+  t.n_end = min(t.n0 + TBN, p.n);
   return t;
 }
 
@@ -301,7 +312,7 @@ __device__ __forceinline__ uint4 codes16(const uint32_t (&d)[4], int lq) {
 // 4 lq .. 4 lq + 3 of subtile j) as bf16 or fp32. Full bf16 tiles store 16
 // bytes per lane (pair16) with one row pointer per subtile row; edge tiles
 // check every row and column.
-template <int KIND, int TM, int TN>
+template <int KIND, int TM, int TN, int TBN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
                                            int64_t row0, int64_t col0) {
   auto put = [&](int64_t row, int64_t col, const v4f& v) {
@@ -311,7 +322,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * p.ldo + col) = pack_bf16x4(v);
     }
   };
-  if (cur.m_end - cur.m0 == BM && cur.n_end - cur.n0 == BN) {   // uniform
+  if (cur.m_end - cur.m0 == BM && cur.n_end - cur.n0 == TBN) {   // uniform
     if constexpr (KIND == KIND_WGRAD) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -404,11 +415,12 @@ __device__ __forceinline__ void store_tile_q(const GemmArgs& p, const Tile& cur,
 
 // Epilogue of a tile: plain store, or (QMODE 1: s = absmax / 448, 2: power of
 // two) with the quantised copy of the output.
-template <int KIND, int QMODE, int TM, int TN>
+template <int KIND, int QMODE, int TM, int TN, int TBN = BN>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
                                          int64_t row0, int64_t n_wave, int lq) {
+  static_assert(QMODE == 0 || TBN == BN, "quantised output: 256-column tiles");
   if constexpr (QMODE == 0)
-    store_tile<KIND, TM, TN>(p, cur, acc, row0, n_wave + 4 * lq);
+    store_tile<KIND, TM, TN, TBN>(p, cur, acc, row0, n_wave + 4 * lq);
   else
     store_tile_q<QMODE == 2, TM, TN>(p, cur, acc, row0, n_wave + 4 * lq, n_wave / 128, lq);
 }
@@ -438,13 +450,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& cur, con
 // cursor on. After the last step the cursor stays put: further loads repeat
 // that step into a stage no one reads any more (the kernels wait for them
 // before they end), which keeps every load unconditional.
-template <int KIND, bool GROUPED, int WAVES, int LOADERS>
+template <int KIND, bool GROUPED, int WAVES, int LOADERS, int TBN = BN>
 struct Loader {
+  using S = Stage<TBN>;
   static constexpr int kRowsPerRound = 8 * LOADERS;      // one dwordx4 load per wave covers 8 rows
-  static constexpr int kRounds = BM / kRowsPerRound;
+  static constexpr int kRounds = BM / kRowsPerRound;     // of A; then kRoundsB of B
+  static constexpr int kRoundsB = TBN / kRowsPerRound;
   static constexpr int kScaleWaves = 8 / WAVES;
-  static constexpr int kParts = 2 * kRounds + kScaleWaves;
-  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0, "load rounds");
+  static constexpr int kParts = kRounds + kRoundsB + kScaleWaves;
+  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0 && TBN % kRowsPerRound == 0,
+                "load rounds");
   static_assert(WAVES == 4 || WAVES == 8, "scale waves");
 
   const GemmArgs& p;
@@ -453,7 +468,7 @@ struct Loader {
   const uint32_t smem_base;
   const int wave, lane;
   const uint32_t lrow, g16;
-  uint32_t voff_a[kRounds], voff_b[kRounds];
+  uint32_t voff_a[kRounds], voff_b[kRoundsB];
   uint32_t s_off[kScaleWaves];
   int64_t s_step[kScaleWaves];
   const float* d_sk[kScaleWaves];
@@ -473,15 +488,14 @@ struct Loader {
       s_step[v] = sw < 4 ? p.ldsa : (KIND == KIND_FPROP ? 1 : p.ldsb);
     }
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      voff_a[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.lda + g16;
-      voff_b[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.ldb + g16;
-    }
+    for (int i = 0; i < kRounds; ++i) voff_a[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.lda + g16;
+#pragma unroll
+    for (int i = 0; i < kRoundsB; ++i) voff_b[i] = ((uint32_t)(i * kRowsPerRound) + lrow) * (uint32_t)p.ldb + g16;
     cursor_tile();
   }
 
   __device__ __forceinline__ void cursor_tile() {
-    const Tile t = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * dtk);
+    const Tile t = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * dtk);
     rs_a = make_rsrc(p.a + t.m0 * p.lda, p.a + (p.m - 1) * p.lda + p.k);
     rs_b = make_rsrc(t.b + t.n0 * p.ldb, t.b + (p.n - 1) * p.ldb + p.k);
 #pragma unroll
@@ -519,26 +533,26 @@ struct Loader {
 
   // Load instruction q of the cursor's step into stage st.
   __device__ __forceinline__ void part(int q, int st) const {
-    const uint32_t base = smem_base + (uint32_t)(st * kStage);
-    if (q < 2 * kRounds) {
+    const uint32_t base = smem_base + (uint32_t)(st * S::kStage);
+    if (q < kRounds + kRoundsB) {
       if constexpr (LOADERS < WAVES) {
         if (wave >= LOADERS) return;
       }
       if (q < kRounds)
         dma16_buf(rs_a, voff_a[q], base + (q * kRowsPerRound + 8 * wave) * BK);
       else
-        dma16_buf(rs_b, voff_b[q - kRounds], base + kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
+        dma16_buf(rs_b, voff_b[q - kRounds], base + S::kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
       return;
     }
-    const int v = q - 2 * kRounds, sw = wave + v * WAVES;
+    const int v = q - kRounds - kRoundsB, sw = wave + v * WAVES;
     // with four waves, scale wave v of wave w is w (activations) or w + 4
     const bool act = WAVES == 4 ? v == 0 : sw < 4;
     if (act || KIND == KIND_WGRAD) {
-      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (act ? kSaOff : kSbOff) + 256 * (sw & 3));
+      dma4(uniform_ptr(d_sk[v]), s_off[v], base + (act ? S::kSaOff : S::kSbOff) + 256 * (sw & 3));
     } else if (sw == 4) {
       // FPROP / DGRAD: the tile's two weight block scales; a load's cost
       // follows its active lanes, so only two lanes take part
-      if (lane < 2) dma4(uniform_ptr(d_sk[v]), s_off[v], base + kSbOff);
+      if (lane < 2) dma4(uniform_ptr(d_sk[v]), s_off[v], base + S::kSbOff);
     }
   }
 };
@@ -547,10 +561,11 @@ struct Loader {
 // walks its tiles (make_walk); the first chunk of the next tile is fetched
 // during the current tile's last chunks, so the pipeline fills once per
 // workgroup.
-template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N, int LOADERS, int QMODE = 0>
-__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
-  using C = Cfg<WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+template <int KIND, bool GROUPED, int WAVES_M, int WAVES_N, int LOADERS, int QMODE = 0, int TBN = BN>
+__global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_kernel(GemmArgs p, GroupArgs g) {
+  using C = Cfg<WAVES_M, WAVES_N, TBN>;
+  using S = Stage<TBN>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -562,7 +577,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   const Walk wk = make_walk(p);
   if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
   const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
-  Loader<KIND, GROUPED, C::kWaves, LOADERS> ld(p, g, wk, lds_addr(smem), wave, lane);
+  Loader<KIND, GROUPED, C::kWaves, LOADERS, TBN> ld(p, g, wk, lds_addr(smem), wave, lane);
   constexpr int kParts = decltype(ld)::kParts;
 
   // LDS byte offset of this lane's operand slice inside a 16-row subtile whose
@@ -575,22 +590,22 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   // activation subtiles, the first weight subtile and the per-row scale
   // products of the chunk.
   auto read_scales = [&](const uint8_t* stage, float (&sc)[C::TM]) {
-    const float* Sa = reinterpret_cast<const float*>(stage + kSaOff);
-    const float* Sb = reinterpret_cast<const float*>(stage + kSbOff);
+    const float* Sa = reinterpret_cast<const float*>(stage + S::kSaOff);
+    const float* Sb = reinterpret_cast<const float*>(stage + S::kSbOff);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
     if constexpr (KIND != KIND_WGRAD) {
-      const float sbv = Sb[wave_n];
+      const float sbv = Sb[wave_n * C::WN / 128];   // the weight block of the wave's columns
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
     }
   };
   auto wgrad_col_scales = [&](const uint8_t* stage, int j) {
-    return *reinterpret_cast<const v4f*>(stage + kSbOff + 4 * (wave_n * C::WN + j * 16 + 4 * lq));
+    return *reinterpret_cast<const v4f*>(stage + S::kSbOff + 4 * (wave_n * C::WN + j * 16 + 4 * lq));
   };
   auto a_frag = [&](const uint8_t* stage, int i) { return frag(stage + (wave_m * C::WM + i * 16) * BK, off0, off1); };
   auto b_frag = [&](const uint8_t* stage, int j) {
-    return frag(stage + kABytes + (wave_n * C::WN + j * 16) * BK, off0, off1);
+    return frag(stage + S::kABytes + (wave_n * C::WN + j * 16) * BK, off0, off1);
   };
 
 #pragma unroll
@@ -609,7 +624,9 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   // it (measured: four columns ahead is 2% faster than three). bw[0] is the current
   // column's, bw[q] the one q columns on; the barrier precedes column kBarCol,
   // the first whose look-ahead read falls into the next step's stage.
-  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : (GROUPED || QMODE != 0 ? 3 : 4);
+  // With four columns per wave (128-column tiles) two columns ahead keep the
+  // barrier mid-step.
+  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : C::TN < 8 ? C::TN / 2 : (GROUPED || QMODE != 0 ? 3 : 4);
   constexpr int kBarCol = C::TN - kBAhead;
   v8i bw[kBAhead + 1];
 #pragma unroll
@@ -657,8 +674,8 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
   for (int tk = 0; tk < my_tiles; ++tk) {
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nc; ++c, ++s) {
-      const uint8_t* stage = smem + (s & 1) * kStage;
-      const uint8_t* nstage = smem + ((s + 1) & 1) * kStage;
+      const uint8_t* stage = smem + (s & 1) * S::kStage;
+      const uint8_t* nstage = smem + ((s + 1) & 1) * S::kStage;
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         if (j == kBarCol) {
@@ -724,8 +741,8 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N>::kThreads)) void gemm_kernel
       fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], sbj[(u / C::TM) & 1]);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
-    const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
-    epilogue<KIND, QMODE, C::TM, C::TN>(p, cur, acc, cur.m0 + wave_m * C::WM + l16, cur.n0 + wave_n * C::WN, lq);
+    const Tile cur = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * tk);
+    epilogue<KIND, QMODE, C::TM, C::TN, TBN>(p, cur, acc, cur.m0 + wave_m * C::WM + l16, cur.n0 + wave_n * C::WN, lq);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -975,7 +992,7 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
 
 GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda, const float* sa,
                    int64_t ldsa, const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                   void* out, int64_t ldo) {
+                   void* out, int64_t ldo, int tbn = BN) {
   GemmArgs p;
   p.m = m; p.n = n; p.k = k;
   p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;
@@ -983,7 +1000,7 @@ GemmArgs make_args(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t ld
   p.out = out; p.ldo = ldo;
   p.q = nullptr; p.ldq = 0; p.sq = nullptr; p.ldsq = 0;
   p.tiles_m = (int)((m + BM - 1) / BM);
-  p.tiles_n = (int)((n + BN - 1) / BN);
+  p.tiles_n = (int)((n + tbn - 1) / tbn);
   return p;
 }
 

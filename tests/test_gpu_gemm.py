@@ -65,6 +65,32 @@ def test_fprop_ragged(m, n, k, seed):
     _fprop_case(x, w, f"ragged {m}x{n}x{k}")
 
 
+# The library runs GEMMs with at most 128 tiles of 256 x 256 on 256 x 128 tiles
+# (the cases above); these have more, so they take the 256 x 256 kernel, with
+# ragged last tiles in both dimensions.
+@pytest.mark.parametrize("m,n,k,seed", [(2100, 4224, 256, 37), (2049, 4480, 384, 38)])
+def test_fprop_ragged_wide_tiles(m, n, k, seed):
+    assert -(-m // 256) * -(-n // 256) > 128
+    x = act(seed, m, k, dist="student_t3", outlier_p=0.002, outlier_mult=20)
+    w = act(seed + 1000, n, k, std=0.02)
+    _fprop_case(x, w, f"ragged wide tiles {m}x{n}x{k}")
+
+
+def test_dgrad_ragged_wide_tiles():
+    m, nw, kw = 2100, 256, 4224
+    assert -(-m // 256) * -(-kw // 256) > 128
+    dy = act(46, m, nw, std=1e-3)
+    w = act(47, nw, kw, std=0.02)
+    log(f"gemm dgrad dY{dy.shape} W{w.shape}")
+    dq, ds = fb.quant_act_1x128(dev_bf16(dy))
+    wq, ws, wqt = fb.quant_w_128x128(dev_bf16(w), transposed_copy=True)
+    dx = fb.gemm(fb.DGRAD, dq, ds, wqt, ws)
+    qd0, sd0 = oq.quant_act_1x128(dy)
+    qw0, sw0 = oq.quant_w_128x128(w)
+    y32, _, ab = og.dgrad(qd0, sd0, qw0, sw0)
+    _assert_ok(check_gemm_bf16(host_bf16_bits(dx), y32, ab), f"dgrad wide tiles {m}x{kw}x{nw}")
+
+
 def test_fprop_zero_and_outlier_rows():
     x = act(35, 256, 512).copy()
     x[:40] = 0                        # zero rows (like MoE padding): s = 0, output exactly 0
