@@ -35,10 +35,11 @@
 //    consecutive rows at one logical slot; measured on gfx950, ds_read_b128
 //    runs at full LDS bandwidth only if rows r and r + 8 also land in different
 //    slots (an (r & 7) swizzle alone halves it).
-//  * Persistent workgroups, one per CU; each XCD (own L2) walks a contiguous
-//    range of output tiles in groups of 8 row-tiles, so the blocks resident on
-//    one XCD share activation and weight panels in its L2. The next tile's
-//    first chunk is fetched during the current tile's last chunk.
+//  * Persistent workgroups, one per CU, walking output tiles in groups of 8
+//    row-tiles; an XCD's 32 workgroups take 32 consecutive tiles at a time
+//    (an 8 x 4 block sharing panels in its L2) and the eight XCDs neighbouring
+//    blocks (sharing panels in the MALL). The next tile's first chunk is
+//    fetched during the current tile's last chunk.
 #pragma once
 
 #include "internal.h"
@@ -232,10 +233,16 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const GroupArgs& g,
 }
 
 // This workgroup's share of the persistent tile walk. Workgroup w runs on XCD
-// w % 8 (hardware round-robin); the tiles of XCD x are a contiguous range of
-// the grouped walk, shared out among that XCD's workgroups, so blocks resident
-// on one XCD (one L2) work on neighbouring tiles. Its tiles are logical
-// indices start + local + nper * t, t = 0 .. my_tiles - 1.
+// x = w % 8 (hardware round-robin) as its local = w / 8-th workgroup. With a
+// grid of 8 C workgroups (C per XCD), the grouped walk is cut into chunks of C
+// consecutive tiles dealt to the XCDs in turn (chunk c to XCD c % 8), one tile
+// per workgroup: at any time the eight XCDs work on eight consecutive chunks,
+// which share operand panels (in the large fprop the same 8 row-tiles of A, in a
+// grouped MoE GEMM mostly one expert's weight) in the MALL. A grid that is not
+// a multiple of 8 (fewer tiles than CUs) gives XCD x a contiguous range of the
+// walk instead. Either way the
+// workgroup's tiles are logical indices start + local + nper * t,
+// t = 0 .. my_tiles - 1.
 struct Walk {
   int start, local, nper, my_tiles, nc, total;
 };
@@ -247,9 +254,17 @@ __device__ __forceinline__ Walk make_walk(const GemmArgs& p) {
   const int x = w % kXcds;
   wk.local = w / kXcds;
   wk.nper = G / kXcds + (x < G % kXcds ? 1 : 0);
-  const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
-  wk.start = x * (T / kXcds) + min(x, T % kXcds);
-  wk.my_tiles = wk.local < count ? (count - wk.local + wk.nper - 1) / wk.nper : 0;
+  if (G % kXcds == 0) {
+    const int C = G / kXcds;
+    wk.start = x * C;
+    wk.nper = kXcds * C;
+    const int first = wk.start + wk.local;
+    wk.my_tiles = first < T ? (T - 1 - first) / wk.nper + 1 : 0;
+  } else {
+    const int count = T / kXcds + (x < T % kXcds ? 1 : 0);
+    wk.start = x * (T / kXcds) + min(x, T % kXcds);
+    wk.my_tiles = wk.local < count ? (count - wk.local + wk.nper - 1) / wk.nper : 0;
+  }
   wk.nc = (int)(p.k / BK);
   wk.total = wk.my_tiles * wk.nc;
   return wk;
