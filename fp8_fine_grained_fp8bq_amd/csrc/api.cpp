@@ -80,7 +80,7 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
   if (mode == FP8BQ_ACT_ROWWISE) {
     if (ldq < cols) return fail(FP8BQ_E_INVAL, "quant_act: ldq < cols");
     if (lds < rows) return fail(FP8BQ_E_INVAL, "quant_act: lds < rows");
-    if (rows >= kMaxTiles || cols / 128 > 65535) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
+    if (rows >= kMaxTiles || (rows + 31) / 32 * (cols / 128) >= kMaxTiles) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
   } else {
     if (rows % 128) return fail(FP8BQ_E_SHAPE, "quant_act: column-wise mode needs rows (%lld) to be a multiple of 128", (long long)rows);
     if (ldq < rows) return fail(FP8BQ_E_INVAL, "quant_act: ldq < rows (transposed output)");

@@ -62,6 +62,9 @@ def test_quant_act_validation(L):
     assert _st(L, f, *ok[:8] + [255, None]) == fb.E_INVAL                       # lds < rows
     assert _st(L, f, *[A16 + 2] + ok[1:]) == fb.E_ALIGN
     assert _st(L, f, *ok[:3] + [1028] + ok[4:]) == fb.E_ALIGN                   # ldx % 8
+    big = 1 << 30                                                               # 2^31 blocks of 32 rows x 128
+    assert _st(L, f, A16, big, 8192, 8192, 0, B16, 8192, S4, big, None) == fb.E_SHAPE
+    assert "too large" in L.fp8bq_last_error().decode()
     col = [A16, 200, 1024, 1024, 1, B16, 256, S4, 1024, None]
     assert _st(L, f, *col) == fb.E_SHAPE                                        # rows % 128 (col-wise)
     col[1] = 256
