@@ -108,7 +108,7 @@ int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq
   if (lds < rows || ldst < cols) return fail(FP8BQ_E_INVAL, "requant_t: lds must be >= rows and ldst >= cols");
   if (rows % 128 || cols % 128)
     return fail(FP8BQ_E_SHAPE, "requant_t: rows (%lld) and cols (%lld) must be multiples of 128", (long long)rows, (long long)cols);
-  if (rows / 128 > 65535 || cols / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "requant_t: too large");
+  if (cols / 128 > 65535 || rows / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "requant_t: too large");
   if (!aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 4) || !aligned(st, 4))
     return fail(FP8BQ_E_ALIGN, "requant_t: q and qt must be 16-byte aligned, scales 4-byte aligned");
   if (ldq % 16 || ldqt % 16) return fail(FP8BQ_E_ALIGN, "requant_t: ldq and ldqt must be multiples of 16");

@@ -105,6 +105,9 @@ def test_requant_validation(L):
     assert bad(6, B16 + 8) == fb.E_ALIGN
     assert bad(3, 392) == fb.E_ALIGN                                            # ldq % 16
     assert bad(8, S4 + 2) == fb.E_ALIGN
+    wide = 128 * 65536                                                          # 65536 column blocks: one past the grid
+    assert _st(L, f, A16, 128, wide, wide, S4, 128, B16, 128, S4 + 4096, wide, 0, None) == fb.E_SHAPE
+    assert "too large" in L.fp8bq_last_error().decode()
 
 
 def _gemm_ok(op=0):
