@@ -58,7 +58,8 @@ def test_fprop_tiny_config():
 
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 128, 128, 31), (300, 384, 640, 32), (513, 256, 256, 33),
-                                         (128, 640, 1152, 34)])
+                                         (128, 640, 1152, 34),
+                                         (1000, 1024, 512, 39)])   # 32 tiles: the grid deals 4-tile chunks to the XCDs
 def test_fprop_ragged(m, n, k, seed):
     x = act(seed, m, k, dist="student_t3", outlier_p=0.002, outlier_mult=20)
     w = act(seed + 1000, n, k, std=0.02)
