@@ -633,16 +633,16 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
   ld.advance();
 
   // Weight fragments are read kBAhead columns before their MFMAs (one column
-  // for WGRAD, whose column scales take the registers; three in the
-  // output-quantising kernel, whose epilogue needs the registers). The earlier
-  // the barrier sits in the step, the less the waves lose waiting at it
-  // (measured: four columns ahead is 2% faster than three; in the grouped
-  // kernel 1.5%, although it then spills one register per step). bw[0] is the current
+  // for WGRAD, whose column scales take the registers). The earlier the
+  // barrier sits in the step, the less the waves lose waiting at it (measured:
+  // four columns ahead is 2% faster than three; in the grouped and the
+  // output-quantising kernels 1.5% and 1%, although they then spill one
+  // register per step). bw[0] is the current
   // column's, bw[q] the one q columns on; the barrier precedes column kBarCol,
   // the first whose look-ahead read falls into the next step's stage.
   // With four columns per wave (128-column tiles) two columns ahead keep the
   // barrier mid-step.
-  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : C::TN < 8 ? C::TN / 2 : (QMODE != 0 ? 3 : 4);
+  constexpr int kBAhead = KIND == KIND_WGRAD ? 1 : C::TN < 8 ? C::TN / 2 : 4;
   constexpr int kBarCol = C::TN - kBAhead;
   v8i bw[kBAhead + 1];
 #pragma unroll
