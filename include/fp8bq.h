@@ -168,6 +168,14 @@ int fp8bq_quant_w_128x128(const void* w, int64_t n, int64_t k, int64_t ldw,
  *                  ldsb >= n (column-wise activation quantisation output).
  * out    FPROP / DGRAD: bf16 [m, n] (round-to-nearest-even), ldo >= n.
  *        WGRAD: float [m, n], ldo >= n.
+ * Scale range (general scales): each chunk's partial sum is multiplied by the
+ *        binary32 product fl32(sa(i,c) * sb(j,c)) and added with one FMA. A
+ *        product below 2^-126 is an fp32 subnormal with fewer significant
+ *        bits; its rounding adds at most |P_c| * 2^-150, so the accuracy bound
+ *        |out - exact| <= 2e-3 * sum_k |a_hat_k||b_hat_k| holds for products
+ *        down to 2^-140 (tested at 2^-135). Smaller products (operand tiles
+ *        whose absmax values multiply to less than about 2^-122) lose accuracy
+ *        gradually; the result is then still finite.
  * op | FP8BQ_SCALE_POW2: every scale of sa and sb is a power of two in
  *        [2^-127, 2^127], as the quantisers write with FP8BQ_SCALE_POW2 (only
  *        the exponent field is read; other scales give wrong results). The

@@ -86,3 +86,30 @@ def check_gemm_f32(y: np.ndarray, y32: np.ndarray, ab: np.ndarray, eps: float = 
         rel = np.where(ab > 0, d / ab, np.where(d == 0, 0.0, np.inf))
     return {"n": int(y.size), "bad": int((d > eps * ab).sum()), "max_rel": float(rel.max()),
             "outside_tight": int((d > TIGHT * ab).sum())}
+
+
+# ---------------------------------------------------------------------------
+# full-size helpers: poison-filled outputs and per-tile row samples
+# ---------------------------------------------------------------------------
+
+def poisoned(shape, fp32: bool = False):
+    """A device buffer of all-ones bits (bf16 / fp32 NaN): never the rounding of a
+    finite sum, so an element the kernel never writes stays recognisable."""
+    import torch
+    return torch.full(shape, -1, dtype=torch.int32 if fp32 else torch.int16, device="cuda")
+
+
+def assert_no_poison(t, fp32: bool = False) -> None:
+    import torch
+    bad = int((t.view(torch.int32 if fp32 else torch.int16) == -1).sum())
+    assert bad == 0, f"{bad} output elements were never written"
+
+
+def tile_rows(m: int, extra: int, seed: int, tile: int = 256, lo: int = 0) -> np.ndarray:
+    """Sorted sample of rows in [lo, m): one random row in every `tile`-row tile of
+    the output (so every tile of the walk is compared somewhere), the first and last
+    rows, and `extra` more."""
+    rng = np.random.default_rng(seed)
+    per_tile = [int(rng.integers(t, min(m, t + tile))) for t in range(lo, m, tile)]
+    more = rng.integers(lo, m, size=extra) if extra > 0 else np.zeros(0, np.int64)
+    return np.unique(np.concatenate([[lo, m - 1], per_tile, more])).astype(np.int64)

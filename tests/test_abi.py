@@ -257,3 +257,40 @@ def test_valid_arguments_without_device_report_e_device(L):
     assert _st(L, "fp8bq_grouped_gemm_decode", 3, (ctypes.c_int64 * 4)(0, 17, 17, 273), 2048, 7168, A16, 7168,
                S4, 512, B16, 7168, S4, 56, O16, 2048, 0, None) == fb.E_DEVICE
     assert "device" in L.fp8bq_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# the probe library (include/fp8bq_probe.h): exports and host-side validation
+# ---------------------------------------------------------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "fp8bq_probe.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    from fp8_fine_grained_fp8bq_amd import probe
+    if not os.path.exists(probe.LIB_PATH):
+        pytest.skip("libfp8bq_probe.so not built (run __graft_entry__.build())")
+    return probe.lib()
+
+
+def test_probe_symbols_exported(P):
+    from fp8_fine_grained_fp8bq_amd import probe
+    text = open(PROBE_HEADER).read()
+    declared = sorted(set(re.findall(r"\b(fp8bq_probe_[a-z0-9_]+)\s*\(", text)))
+    assert declared and set(declared) == set(probe.EXPORTS)
+    for name in declared:
+        assert hasattr(P, name), name
+
+
+def test_probe_validation(P):
+    assert P.fp8bq_probe_mfma_accum(None, B16, 4096, S4, S4, None) == fb.E_INVAL
+    assert P.fp8bq_probe_mfma_accum(A16, B16, 4000, S4, S4, None) == fb.E_SHAPE
+    assert P.fp8bq_probe_mfma_accum(A16, B16, 0, S4, S4, None) == fb.E_SHAPE
+    assert P.fp8bq_probe_mfma_accum(A16 + 4, B16, 4096, S4, S4, None) == fb.E_ALIGN
+    assert P.fp8bq_probe_mfma_once(A16, None, S4, S4, None) == fb.E_INVAL
+    assert P.fp8bq_probe_mfma_once(A16, B16 + 8, S4, S4, None) == fb.E_ALIGN
+    assert P.fp8bq_probe_mfma_stream(1, 0, 256, A16, S4, S4, S4, None) == fb.E_INVAL
+    assert P.fp8bq_probe_mfma_stream(1, 16, 0, A16, S4, S4, S4, None) == fb.E_INVAL
+    assert P.fp8bq_probe_mfma_stream(1, 16, 256, A16 + 1, S4, S4, S4, None) == fb.E_ALIGN
+    assert "aligned" in P.fp8bq_probe_last_error().decode()

@@ -16,7 +16,8 @@ import pytest
 import fp8_fine_grained_fp8bq_amd as fb
 from oracle import gemm as og
 from oracle import quant as oq
-from tests.gpu_util import check_gemm_bf16, check_gemm_f32, dev_bf16, host, host_bf16_bits, log
+from tests.gpu_util import (assert_no_poison, check_gemm_bf16, check_gemm_f32, dev_bf16, host,
+                            host_bf16_bits, log, poisoned, tile_rows)
 from workloads import act, backward_dy, dense_fprop, large_fprop, moe_fprop, tiny_fprop
 
 pytestmark = pytest.mark.gpu
@@ -34,9 +35,12 @@ def _assert_ok(stats, name):
 
 
 def _fprop_case(xbits, wbits, name, rows=None):
+    import torch
     log(f"gemm fprop {name} X{xbits.shape} W{wbits.shape}")
     xq, xs, wq, ws, _ = _quant_pair_fprop(xbits, wbits)
-    y = fb.gemm(fb.FPROP, xq, xs, wq, ws)
+    y = poisoned((xbits.shape[0], wbits.shape[0]))
+    fb.gemm(fb.FPROP, xq, xs, wq, ws, out=y.view(torch.bfloat16))
+    assert_no_poison(y)
     qx0, sx0 = oq.quant_act_1x128(xbits if rows is None else xbits[rows])
     qw0, sw0 = oq.quant_w_128x128(wbits)
     xq_h, xs_h = host(xq), host(xs).T
@@ -90,6 +94,25 @@ def test_dgrad_ragged_wide_tiles():
     qw0, sw0 = oq.quant_w_128x128(w)
     y32, _, ab = og.dgrad(qd0, sd0, qw0, sw0)
     _assert_ok(check_gemm_bf16(host_bf16_bits(dx), y32, ab), f"dgrad wide tiles {m}x{kw}x{nw}")
+
+
+def test_dgrad_tiny_scale_products():
+    # dY tiles near 2^-116 against ordinary weights: s_dY * s_W is about 2^-135, an
+    # fp32 subnormal with 15 significant bits, inside the documented range (>= 2^-140)
+    m, nw, kw = 256, 256, 512
+    dy = act(48, m, nw, std=2.0 ** -116)
+    w = act(49, nw, kw, std=0.02)
+    log(f"gemm dgrad tiny scales dY{dy.shape} W{w.shape}")
+    dq, ds = fb.quant_act_1x128(dev_bf16(dy))
+    wq, ws, wqt = fb.quant_w_128x128(dev_bf16(w), transposed_copy=True)
+    qd0, sd0 = oq.quant_act_1x128(dy)
+    qw0, sw0 = oq.quant_w_128x128(w)
+    np.testing.assert_array_equal(host(dq), qd0)
+    prod = sd0.astype(np.float64).min() * sw0.astype(np.float64).min()
+    assert 2.0 ** -140 <= prod < 2.0 ** -126, prod
+    dx = fb.gemm(fb.DGRAD, dq, ds, wqt, ws)
+    y32, _, ab = og.dgrad(qd0, sd0, qw0, sw0)
+    _assert_ok(check_gemm_bf16(host_bf16_bits(dx), y32, ab), "dgrad with subnormal scale products")
 
 
 def test_fprop_zero_and_outlier_rows():
@@ -169,17 +192,14 @@ def test_grouped_single_group_equals_fprop_layout():
 
 
 # ---------------------------------------------------------------------------
-# full sizes: every quantised byte is checked, the GEMM on sampled rows
+# full sizes: every quantised byte is checked; the GEMM output is poison-filled
+# first (no element may stay unwritten) and compared with the oracle on sampled
+# rows, at least one in every 256-row tile of the walk
 # ---------------------------------------------------------------------------
-
-def _sample_rows(m, count, seed):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, m - 1], rng.choice(m, size=count, replace=False)]))
-
 
 def test_dense_fprop_full_size():
     cfg = dense_fprop()
-    rows = _sample_rows(cfg.x.shape[0], 48, 61)
+    rows = tile_rows(cfg.x.shape[0], 32, 61)
     _fprop_case(cfg.x, cfg.w, "dense 4096x2048x7168 (sampled rows)", rows=rows)
 
 
@@ -187,10 +207,13 @@ def test_backward_pair_full_size():
     dense = dense_fprop()
     dy = backward_dy()                                   # [4096, 2048]
     log("backward pair full size: dgrad 4096x7168x2048, wgrad 2048x7168x4096")
+    import torch
     dq, ds = fb.quant_act_1x128(dev_bf16(dy))
     wq, ws, wqt = fb.quant_w_128x128(dev_bf16(dense.w), transposed_copy=True)
-    dx = fb.gemm(fb.DGRAD, dq, ds, wqt, ws)
-    rows = _sample_rows(4096, 24, 62)
+    dx = poisoned((4096, 7168))
+    fb.gemm(fb.DGRAD, dq, ds, wqt, ws, out=dx.view(torch.bfloat16))
+    assert_no_poison(dx)
+    rows = tile_rows(4096, 16, 62)
     qd0, sd0 = oq.quant_act_1x128(dy[rows])
     qw0, sw0 = oq.quant_w_128x128(dense.w)
     np.testing.assert_array_equal(host(wqt), qw0.T)
@@ -199,16 +222,18 @@ def test_backward_pair_full_size():
 
     dqt, dst = fb.quant_act_1x128(dev_bf16(dy), fb.ACT_COLWISE)        # [2048, 4096]
     xqt, xst = fb.quant_act_1x128(dev_bf16(dense.x), fb.ACT_COLWISE)   # [7168, 4096]
-    dw = fb.gemm(fb.WGRAD, dqt, dst, xqt, xst)
+    dw = poisoned((2048, 7168), fp32=True)
+    fb.gemm(fb.WGRAD, dqt, dst, xqt, xst, out=dw.view(torch.float32))
+    assert_no_poison(dw, fp32=True)
     qd0, sd0 = oq.quant_act_128x1(dy)
     np.testing.assert_array_equal(host(dqt), qd0)
     np.testing.assert_array_equal(host(dst).T, sd0)
-    rows = _sample_rows(2048, 16, 63)
-    cols = np.sort(np.random.default_rng(64).choice(7168, size=512, replace=False))
+    rows = tile_rows(2048, 8, 63)
+    cols = tile_rows(7168, 480, 64)          # every 256-column tile as well
     qx0, sx0 = oq.quant_act_128x1(dense.x[:, cols])
     np.testing.assert_array_equal(host(xqt)[cols], qx0)
     y32, _, ab = og.wgrad(qd0[rows], sd0[rows], qx0, sx0)
-    _assert_ok(check_gemm_f32(host(dw)[np.ix_(rows, cols)], y32, ab), "wgrad full (sampled)")
+    _assert_ok(check_gemm_f32(host(dw).view(np.float32)[np.ix_(rows, cols)], y32, ab), "wgrad full (sampled)")
 
 
 def test_moe_grouped_full_size():
@@ -223,13 +248,15 @@ def test_moe_grouped_full_size():
         q, s, _ = fb.quant_w_128x128(dev_bf16(cfg.w[e]))
         wq[e].copy_(q)
         wsd[e].copy_(s)
-    y = fb.grouped_gemm(cfg.row_off, xq, xs, wq, wsd)
+    y = poisoned((int(cfg.row_off[-1]), 2048))
+    fb.grouped_gemm(cfg.row_off, xq, xs, wq, wsd, out=y.view(torch.bfloat16))
+    assert_no_poison(y)
     yb = host_bf16_bits(y)
-    rng = np.random.default_rng(65)
     for e in range(G):
         r0, r1 = int(cfg.row_off[e]), int(cfg.row_off[e + 1])
         real = r0 + int(cfg.real_rows[e])
-        rows = np.unique(np.concatenate([[r0, real - 1], rng.integers(r0, real, 6)]))
+        # one row in every 256-row tile of the expert that holds routed rows
+        rows = tile_rows(real, 2, 65 + e, lo=r0)
         qx0, sx0 = oq.quant_act_1x128(cfg.x[rows])
         qw0, sw0 = oq.quant_w_128x128(cfg.w[e])
         y32, _, ab = og.fprop(qx0, sx0, qw0, sw0)
@@ -238,11 +265,18 @@ def test_moe_grouped_full_size():
 
 
 def test_large_fprop_full_size_sampled():
+    import torch
     cfg = large_fprop()
-    rows = _sample_rows(cfg.x.shape[0], 24, 66)
-    log("large fprop 16384x18432x7168 (sampled rows)")
+    rows = tile_rows(cfg.x.shape[0], 8, 66)
+    log("large fprop 16384x18432x7168 (sampled rows, one in every row tile)")
     xq, xs, wq, ws, _ = _quant_pair_fprop(cfg.x, cfg.w)
-    y = fb.gemm(fb.FPROP, xq, xs, wq, ws)
+    y = poisoned((16384, 18432))
+    fb.gemm(fb.FPROP, xq, xs, wq, ws, out=y.view(torch.bfloat16))
+    assert_no_poison(y)
+    # a second launch gives the same bytes (the kernel fixes its summation order)
+    y2 = fb.gemm(fb.FPROP, xq, xs, wq, ws)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "repeated launches differ"
+    del y2
     qx0, sx0 = oq.quant_act_1x128(cfg.x[rows])
     np.testing.assert_array_equal(host(xq)[rows], qx0)
     np.testing.assert_array_equal(host(xs).T[rows], sx0)
