@@ -40,7 +40,9 @@ def test_tiny_config_rowwise():
 
 
 @pytest.mark.parametrize("rows,cols,ldx,seed", [
-    (1, 128, None, 1), (37, 384, None, 2), (257, 1024, 1088, 3), (64, 7168, None, 4), (3, 256, 264, 5)])
+    (1, 128, None, 1), (37, 384, None, 2), (257, 1024, 1088, 3), (64, 7168, None, 4), (3, 256, 264, 5),
+    # 9 and 17 tiles per row: partial last 8-tile segment; 33 and 130 rows: partial last 32-row block
+    (33, 1152, 1160, 6), (130, 2176, None, 8)])
 def test_ragged_rowwise(rows, cols, ldx, seed):
     x = act(seed, rows, cols, dist="student_t3", outlier_p=0.003, outlier_mult=40)
     _assert_act_rows(x, ldx=ldx, name=f"seed {seed}")
@@ -141,10 +143,13 @@ def _assert_w(bits, ldw=None, with_qt=True, name=""):
     del torch
 
 
+# with the transposed copy and without (one 128x128 block per workgroup, or two
+# neighbouring blocks along k; odd block counts leave the last workgroup half empty)
+@pytest.mark.parametrize("with_qt", [True, False])
 @pytest.mark.parametrize("n,k,ldw,seed", [(128, 128, None, 21), (256, 384, None, 22), (384, 256, 320, 23),
-                                           (2048, 7168, None, 24)])
-def test_quant_w(n, k, ldw, seed):
-    _assert_w(act(seed, n, k, std=0.02), ldw=ldw, name=f"seed {seed}")
+                                           (2048, 7168, None, 24), (640, 1152, 1160, 26)])
+def test_quant_w(n, k, ldw, seed, with_qt):
+    _assert_w(act(seed, n, k, std=0.02), ldw=ldw, with_qt=with_qt, name=f"seed {seed}")
 
 
 def test_quant_w_edge_blocks():
