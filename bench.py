@@ -12,7 +12,11 @@ W bf16 [18432, 7168] ~ N(0, 0.02), Y bf16 [16384, 18432].
 Prints one JSON line: value = 2 M N K / step time (TFLOP/s including both
 quantisers), plus the GEMM kernel's roofline (HIP-event time of the kernel
 alone, on the stream it runs on) and the CPU oracle timed on a bounded sample
-of the same workload.
+of the same workload. Kernels timed alone report the mean, median, p10 and p90
+of --kernel-reps launches; the quantisers are also compared with the measured
+streaming ceiling of their traffic (2 bytes read, 1 written per element), and
+the probes measure what the promotion costs the matrix unit (clock) and how the
+unit accumulates (report section 3.3.2's K = 4096 experiment).
 """
 
 from __future__ import annotations
@@ -47,7 +51,8 @@ def parse():
                     help="untimed steps run back to back for this long before the warm-up steps: the GPU's "
                          "clock needs tens of milliseconds of sustained load to reach its steady state")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="large")
-    ap.add_argument("--kernel-reps", type=int, default=10, help="reps of each kernel timed alone")
+    ap.add_argument("--kernel-reps", type=int, default=50, help="reps of each kernel timed alone")
+    ap.add_argument("--no-probes", action="store_true", help="skip the ceilings and the matrix-unit probes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip timing the dense, backward and MoE configurations' kernels")
@@ -75,21 +80,64 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemm_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the GEMM source has
-    changed since the counters were taken (or the summary is missing)."""
+# every file whose change alters the GEMM kernel's code (the counters taken for one
+# build do not describe another)
+GEMM_SOURCES = ["fp8_fine_grained_fp8bq_amd/csrc/gemm_kernels.h", "fp8_fine_grained_fp8bq_amd/csrc/gemm.hip",
+                "fp8_fine_grained_fp8bq_amd/csrc/fp8_codec.h", "fp8_fine_grained_fp8bq_amd/csrc/internal.h",
+                "fp8_fine_grained_fp8bq_amd/build.py"]
+
+
+def gemm_sources_sha256() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", "large_fprop_hbm_traffic.md")
-    src = os.path.join(ROOT, "fp8_fine_grained_fp8bq_amd", "csrc", "gemm_kernels.h")
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        h.update(rel.encode())
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
+def profile_values(name: str) -> dict:
+    """Machine-readable `key: value` lines of a committed rocprofv3 summary, or {}
+    when the GEMM sources have changed since it was taken (or it is missing)."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith("gemm_") and ": " in line)
-        if kv.get("gemm_source_sha256", "").strip() != hashlib.sha256(open(src, "rb").read()).hexdigest():
-            return None
+    except OSError:
+        return {}
+    if kv.get("gemm_sources_sha256", "").strip() != gemm_sources_sha256():
+        return {}
+    return kv
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when stale or missing."""
+    kv = profile_values("large_fprop_hbm_traffic.md")
+    try:
         return int(kv["gemm_fetch_bytes_per_launch"]) + int(kv["gemm_write_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except (KeyError, ValueError):
         return None
+
+
+def gemm_clock_ghz():
+    """Shader clock under the GEMM from the committed counter summary
+    (GRBM_GUI_ACTIVE per XCD / kernel duration), or None when stale or missing."""
+    kv = profile_values("large_fprop_mfma_counters.md")
+    try:
+        return float(kv["gemm_clock_ghz"])
+    except (KeyError, ValueError):
+        return None
+
+
+def stats(durs):
+    d = np.asarray(durs, dtype=np.float64)
+    return {"mean": float(d.mean()), "median": float(np.median(d)), "p10": float(np.percentile(d, 10)),
+            "p90": float(np.percentile(d, 90)), "n": int(d.size)}
+
+
+def rnd(st, nd=2):
+    return {k: (round(v, nd) if isinstance(v, float) else v) for k, v in st.items()}
 
 
 def cpu_threads() -> int:
@@ -209,16 +257,24 @@ def main():
     # Warm short kernels (batch=True) are timed by one event pair around all reps:
     # a pair around each launch adds 6-13 us of dispatch gap to a 60-90 us kernel.
     def time_kernel(fn, reps, cold, batch=False):
+        fn()                        # first touch of any buffer it writes happens outside the timing
         settle(min(150.0, args.settle_ms))
         if batch and not cold:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                fn()
-            b.record(stream)
+            # ten groups of back-to-back launches, one event pair per group: the
+            # statistics are over group means
+            groups, per = 10, max(1, reps // 10)
+            evs = []
+            for _ in range(groups):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(per):
+                    fn()
+                b.record(stream)
+                evs.append((a, b))
             torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / reps
-            return us, us
+            st = stats([a.elapsed_time(b) * 1e3 / per for a, b in evs])
+            st["launches_per_sample"] = per
+            return st
         evs = []
         for _ in range(reps):
             if cold:
@@ -229,8 +285,7 @@ def main():
             b.record(stream)
             evs.append((a, b))
         torch.cuda.synchronize()
-        durs = [a.elapsed_time(b) * 1e3 for a, b in evs]
-        return float(np.mean(durs)), float(np.median(durs))
+        return stats([a.elapsed_time(b) * 1e3 for a, b in evs])
 
     # power-of-two variant: the same number of timed steps
     for _ in range(args.warmup):
@@ -242,7 +297,8 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_step_p2 = ev0.elapsed_time(ev1) / args.steps
-    tg_p2, _ = time_kernel(gemm_p2, args.kernel_reps, False)
+    st_tg_p2 = time_kernel(gemm_p2, args.kernel_reps, False)
+    tg_p2 = st_tg_p2["mean"]
     log(f"[bench] power-of-two scales: {ms_step_p2:.3f} ms/step, GEMM {tg_p2:.1f} us")
 
     # transposing re-quantisation (1x128 -> 128x1) of the power-of-two cache of X
@@ -255,7 +311,8 @@ def main():
                                  0, sp)
 
     requant()
-    t_rq, _ = time_kernel(requant, args.kernel_reps, True)
+    st_t_rq = time_kernel(requant, args.kernel_reps, True)
+    t_rq = st_t_rq["mean"]
     bytes_rq = 2 * M * K + 2 * (M * (K // 128) * 4)
     log(f"[bench] requant 1x128 -> 128x1: {t_rq:.1f} us ({bytes_rq / t_rq / 1e3:.0f} GB/s)")
 
@@ -276,8 +333,10 @@ def main():
     quant_w()
     gemm_quant_out()
     gemm_then_quant()
-    t_fq, _ = time_kernel(gemm_quant_out, args.kernel_reps, False)
-    t_sq, _ = time_kernel(gemm_then_quant, args.kernel_reps, False)
+    st_t_fq = time_kernel(gemm_quant_out, args.kernel_reps, False)
+    t_fq = st_t_fq["mean"]
+    st_t_sq = time_kernel(gemm_then_quant, args.kernel_reps, False)
+    t_sq = st_t_sq["mean"]
     log(f"[bench] GEMM + output quantisation: fused {t_fq:.1f} us, separate {t_sq:.1f} us")
 
     # decode-shape grouped Fprop (memory-bound): 256 tokens routed top-8, the 8 local
@@ -300,7 +359,8 @@ def main():
                                      d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d, 0, sp)
 
     decode()
-    t_dec, _ = time_kernel(decode, args.kernel_reps, True)
+    st_t_dec = time_kernel(decode, args.kernel_reps, True)
+    t_dec = st_t_dec["mean"]
     bytes_dec = (G_d * N_d * K_d + G_d * (N_d // 128) * (K_d // 128) * 4 + m_d * K_d + m_d * (K_d // 128) * 4
                  + m_d * N_d * 2)
     log(f"[bench] decode grouped Fprop ({m_d} rows): {t_dec:.1f} us ({bytes_dec / t_dec / 1e3:.0f} GB/s)")
@@ -352,21 +412,31 @@ def main():
 
         for fn in (o_fprop, o_dgrad, o_qcol_dy, o_qcol_x, o_wgrad):
             fn()
-        t_of, _ = time_kernel(o_fprop, args.kernel_reps, False, batch=True)
-        t_od, _ = time_kernel(o_dgrad, args.kernel_reps, False, batch=True)
-        t_ow, _ = time_kernel(o_wgrad, args.kernel_reps, False, batch=True)
-        t_qc, _ = time_kernel(o_qcol_x, args.kernel_reps, True)
+        st_t_of = time_kernel(o_fprop, args.kernel_reps, False, batch=True)
+        t_of = st_t_of["mean"]
+        st_t_od = time_kernel(o_dgrad, args.kernel_reps, False, batch=True)
+        t_od = st_t_od["mean"]
+        st_t_ow = time_kernel(o_wgrad, args.kernel_reps, False, batch=True)
+        t_ow = st_t_ow["mean"]
+        st_t_qc = time_kernel(o_qcol_x, args.kernel_reps, True)
+        t_qc = st_t_qc["mean"]
         f_d = 2.0 * Md * Nd * Kd
         b_qc = Md * Kd * 3 + (Md // 128) * Kd * 4
         others["dense_fprop"] = {"what": f"GEMM {Md}x{Nd}x{Kd} (bf16 out)", "us": round(t_of, 2),
-                                 "TFLOPs": round(f_d / (t_of * 1e-6) / 1e12, 1)}
+                                 "TFLOPs": round(f_d / (t_of * 1e-6) / 1e12, 1),
+                                 "frac_fp8_peak": round(f_d / (t_of * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                 "us_stats": rnd(st_t_of)}
         others["dgrad"] = {"what": f"dX = dY W: GEMM {Md}x{Kd}x{Nd} (bf16 out)", "us": round(t_od, 2),
-                           "TFLOPs": round(f_d / (t_od * 1e-6) / 1e12, 1)}
+                           "TFLOPs": round(f_d / (t_od * 1e-6) / 1e12, 1),
+                           "frac_fp8_peak": round(f_d / (t_od * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                           "us_stats": rnd(st_t_od)}
         others["wgrad"] = {"what": f"dW = dY^T X: GEMM {Nd}x{Kd}x{Md} over tokens, 128x1-quantised operands (fp32 out)",
-                           "us": round(t_ow, 2), "TFLOPs": round(f_d / (t_ow * 1e-6) / 1e12, 1)}
+                           "us": round(t_ow, 2), "TFLOPs": round(f_d / (t_ow * 1e-6) / 1e12, 1),
+                           "frac_fp8_peak": round(f_d / (t_ow * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                           "us_stats": rnd(st_t_ow)}
         others["quant_act_128x1"] = {"what": f"token-direction (128x1) quantisation of X [{Md}, {Kd}], transposed out",
                                      "us": round(t_qc, 2), "GBps": round(b_qc / t_qc / 1e3, 1),
-                                     "frac_hbm": round(b_qc / t_qc / 1e3 / PEAK_HBM_GBS, 4)}
+                                     "frac_hbm": round(b_qc / t_qc / 1e3 / PEAK_HBM_GBS, 4), "us_stats": rnd(st_t_qc)}
         del o_x, o_w, o_dy, o_y, o_dx, o_dw
         # MoE grouped fprop (8 local experts, Zipf top-8 routing, rows padded to 128)
         G_m, N_m, K_m = moe.w.shape
@@ -386,25 +456,121 @@ def main():
                                   K_m, g_ws.data_ptr(), K_m // 128, g_y.data_ptr(), N_m, 0, sp)
 
         o_grouped()
-        t_og, _ = time_kernel(o_grouped, args.kernel_reps, False, batch=True)
+        st_t_og = time_kernel(o_grouped, args.kernel_reps, False, batch=True)
+        t_og = st_t_og["mean"]
         f_real = 2.0 * float(np.sum(moe.real_rows)) * N_m * K_m
         others["moe_grouped"] = {"what": f"{moe.name}: {m_m} rows padded to 128 per expert "
                                          f"({int(np.sum(moe.real_rows))} routed)",
                                  "us": round(t_og, 2), "TFLOPs_routed_rows": round(f_real / (t_og * 1e-6) / 1e12, 1),
-                                 "TFLOPs_padded_rows": round(2.0 * m_m * N_m * K_m / (t_og * 1e-6) / 1e12, 1)}
+                                 "TFLOPs_padded_rows": round(2.0 * m_m * N_m * K_m / (t_og * 1e-6) / 1e12, 1),
+                                 "frac_fp8_peak_routed": round(f_real / (t_og * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                 "us_stats": rnd(st_t_og)}
         log(f"[bench] other configs: dense {t_of:.1f} us, dgrad {t_od:.1f} us, wgrad {t_ow:.1f} us, "
             f"128x1 quant {t_qc:.1f} us, MoE grouped {t_og:.1f} us")
 
-    tq_x, _ = time_kernel(quant_x, args.kernel_reps, True)
-    tq_w, _ = time_kernel(quant_w, args.kernel_reps, True)
-    tg, tg_med = time_kernel(gemm, args.kernel_reps, False)
+    st_tq_x = time_kernel(quant_x, args.kernel_reps, True)
+    tq_x = st_tq_x["mean"]
+    st_tq_w = time_kernel(quant_w, args.kernel_reps, True)
+    tq_w = st_tq_w["mean"]
+    st_tg = time_kernel(gemm, args.kernel_reps, False)
+    tg = st_tg["mean"]
     bytes_qx = M * K * 3 + M * (K // 128) * 4
     bytes_qw = N * K * 3 + (N // 128) * (K // 128) * 4
     gemm_tflops = flops / (tg * 1e-6) / 1e12
     log(f"[bench] quant X {tq_x:.1f} us ({bytes_qx / tq_x / 1e3:.0f} GB/s), quant W {tq_w:.1f} us "
         f"({bytes_qw / tq_w / 1e3:.0f} GB/s), GEMM {tg:.1f} us ({gemm_tflops:.0f} TFLOP/s)")
 
+    # measured ceilings of the quantisers' traffic (cold): a stream reading 2 bytes and
+    # writing 1 per element with no arithmetic, and the runtime's device copy
+    ceilings, probes = {}, {}
+    if not args.no_probes:
+        from fp8_fine_grained_fp8bq_amd import probe
+        qbuf = torch.empty((N, K), dtype=torch.uint8, device=dev)
+
+        def stream_x():
+            probe.fp8bq_probe_stream_2to1(x.data_ptr(), qbuf.data_ptr(), M * K, sp)
+
+        def stream_w():
+            probe.fp8bq_probe_stream_2to1(w.data_ptr(), qbuf.data_ptr(), N * K, sp)
+
+        cbuf = torch.empty_like(x)
+
+        def copy_x():
+            cbuf.copy_(x)
+
+        st_sx = time_kernel(stream_x, args.kernel_reps, True)
+        st_sw = time_kernel(stream_w, args.kernel_reps, True)
+        st_cp = time_kernel(copy_x, args.kernel_reps, True)
+        ceilings = {
+            "stream_2to1_X": {"what": f"read 2 B / write 1 B per element over X [{M}, {K}], no arithmetic, cold",
+                              "us": round(st_sx["mean"], 2), "GBps": round(M * K * 3 / st_sx["mean"] / 1e3, 1),
+                              "us_stats": rnd(st_sx)},
+            "stream_2to1_W": {"what": f"read 2 B / write 1 B per element over W [{N}, {K}], no arithmetic, cold",
+                              "us": round(st_sw["mean"], 2), "GBps": round(N * K * 3 / st_sw["mean"] / 1e3, 1),
+                              "us_stats": rnd(st_sw)},
+            "device_copy_X": {"what": f"device-to-device copy of X ({M * K * 2 / 1e6:.0f} MB read + written), cold",
+                              "us": round(st_cp["mean"], 2), "GBps": round(M * K * 4 / st_cp["mean"] / 1e3, 1),
+                              "us_stats": rnd(st_cp)},
+        }
+        del qbuf, cbuf
+        log(f"[bench] ceilings: stream 2:1 X {ceilings['stream_2to1_X']['GBps']} GB/s, "
+            f"W {ceilings['stream_2to1_W']['GBps']} GB/s, copy {ceilings['device_copy_X']['GBps']} GB/s")
+
+        # what the promotion costs the matrix unit: the same MFMA stream with and without
+        # the four FMAs per instruction, the unit kept busy in both (time = clock)
+        quant_x()
+        codes = xq.view(-1)[: 1 << 22].clone()      # 4 MiB of the workload's own E4M3 codes
+        pscales = torch.full((64,), 1e-3, dtype=torch.float32, device=dev)
+        sink = torch.empty((256 * 512,), dtype=torch.float32, device=dev)
+        ticks = torch.zeros((512,), dtype=torch.int64, device=dev)
+        iters = 20000
+        pw = {}
+        for fold in (0, 1, 0, 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            probe.fp8bq_probe_mfma_stream(fold, iters, 256, codes.data_ptr(), pscales.data_ptr(), sink.data_ptr(),
+                                          ticks.data_ptr(), sp)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3
+            tk = ticks.cpu().numpy().reshape(256, 2).astype(np.float64)
+            pw[fold] = {"us": round(us, 1),
+                        "TFLOPs": round(2.0 * 16 * 16 * 128 * 32 * 8 * 256 * iters / (us * 1e-6) / 1e12, 1),
+                        "shader_clock_ghz": round(float(tk[:, 0].sum() / tk[:, 1].sum()) * 0.1, 3)}
+        probes["promotion_power"] = {
+            "what": "256 workgroups x 8 waves, each 20000 x 32 independent 16x16x128 FP8 MFMAs on register-resident "
+                    "fragments; with_fold adds the exact-scale GEMM's promotion (4 FMAs per MFMA)",
+            "mfma_only": pw[0], "with_fold": pw[1],
+            "time_ratio": round(pw[1]["us"] / pw[0]["us"], 4),
+            "clock_note": "shader clock = s_memtime ticks / s_memrealtime ticks x 0.1 GHz",
+        }
+        del codes, sink
+        # accumulation inside the unit against promotion (report section 3.3.2): two
+        # random 16 x 4096 E4M3 matrices, errors against the exact integer dot product
+        from oracle import e4m3 as oe
+        rng = np.random.default_rng(7)
+        ah = [oe.encode((r * (448.0 / np.abs(r).max())).astype(np.float32)) for r in
+              (rng.standard_normal((16, 4096)), rng.standard_normal((16, 4096)))]
+        da, db = torch.from_numpy(ah[0]).to(dev), torch.from_numpy(ah[1]).to(dev)
+        ch = torch.empty((16, 16), dtype=torch.float32, device=dev)
+        pr = torch.empty((16, 16), dtype=torch.float32, device=dev)
+        probe.fp8bq_probe_mfma_accum(da.data_ptr(), db.data_ptr(), 4096, ch.data_ptr(), pr.data_ptr(), sp)
+        torch.cuda.synchronize()
+        ia, ib = (np.round(oe.decode(a_) * 512.0).astype(np.int64) for a_ in ah)
+        exact = (ia @ ib.T).astype(np.float64) * 2.0 ** -18
+        absum = (np.abs(ia) @ np.abs(ib).T).astype(np.float64) * 2.0 ** -18
+        acc = {}
+        for nm, t in (("chained_in_unit", ch), ("promoted_every_128", pr)):
+            err = np.abs(t.cpu().numpy().astype(np.float64) - exact)
+            acc[nm] = {"max_err_over_sum_abs": float((err / absum).max()),
+                       "max_rel_err": float((err[exact != 0] / np.abs(exact[exact != 0])).max())}
+        probes["accumulation_k4096"] = {"what": "16x16x4096 product of two random E4M3 matrices (N(0,1) scaled to "
+                                                "448): inside the matrix unit vs promoted every 128 K", **acc}
+        log(f"[bench] probes: MFMA stream {pw[0]['TFLOPs']} TFLOP/s at {pw[0]['shader_clock_ghz']} GHz, with "
+            f"promotion {pw[1]['TFLOPs']} at {pw[1]['shader_clock_ghz']} GHz; accumulation {acc}")
+
     cpu = None
+    cpu_configs = {}
     if not args.no_cpu_baseline:
         from oracle import gemm as og
         from oracle import quant as oq
@@ -420,7 +586,45 @@ def main():
                "sample": f"quantise X[:{r}] (1x128) and W[:{nw}] (128x128), then the oracle GEMM of "
                          f"those {r}x{nw}x{K} (fp64 chunk sums, fp32 promotion); {csec:.1f} s on the host"}
         log(f"[bench] oracle sample: {csec:.1f} s -> {cpu['value'] * 1e3:.3f} GFLOP/s")
+        # the oracle on a bounded sample of each other configuration: its quantisers (GB/s
+        # of algorithmic bytes) and its GEMM (fp64 chunk sums, GFLOP/s)
+        if others:
+            def timed(fn, *a):
+                c = time.perf_counter()
+                out_ = fn(*a)
+                return out_, time.perf_counter() - c
 
+            dn = workloads.dense_fprop()
+            dyb = workloads.backward_dy()
+            rows = 512
+            (qd, sd), tqa = timed(oq.quant_act_1x128, dn.x[:rows])
+            (qwd, swd), tqw = timed(oq.quant_w_128x128, dn.w)
+            _, tgf = timed(og.fprop, qd, sd, qwd, swd)
+            cpu_configs["dense_fprop"] = {
+                "sample": f"X[:{rows}] of [4096, 7168], all of W [2048, 7168]",
+                "quant_act_GBps": round(rows * 7168 * 3.031 / tqa / 1e9, 3),
+                "quant_w_GBps": round(2048 * 7168 * 3.0 / tqw / 1e9, 3),
+                "gemm_GFLOPs": round(2.0 * rows * 2048 * 7168 / tgf / 1e9, 2)}
+            (qy, sy), _ = timed(oq.quant_act_1x128, dyb[:rows])
+            _, tdg = timed(og.dgrad, qy, sy, qwd, swd)
+            (qyt, syt), tqc = timed(oq.quant_act_128x1, dyb[:, :256])
+            (qxt, sxt), _ = timed(oq.quant_act_128x1, dn.x[:, :512])
+            _, twg = timed(og.wgrad, qyt, syt, qxt, sxt)
+            cpu_configs["backward_pair"] = {
+                "sample": f"Dgrad on dY[:{rows}]; Wgrad dW[:256, :512] over all 4096 tokens",
+                "dgrad_GFLOPs": round(2.0 * rows * 7168 * 2048 / tdg / 1e9, 2),
+                "quant_act_128x1_GBps": round(4096 * 256 * 3.031 / tqc / 1e9, 3),
+                "wgrad_GFLOPs": round(2.0 * 256 * 512 * 4096 / twg / 1e9, 2)}
+            mo = workloads.moe_fprop()
+            e0r = int(mo.real_rows[0])
+            (qm, sm_), _ = timed(oq.quant_act_1x128, mo.x[:rows])
+            (qwm, swm), _ = timed(oq.quant_w_128x128, mo.w[0])
+            _, tmg = timed(og.fprop, qm, sm_, qwm, swm)
+            cpu_configs["moe_grouped"] = {"sample": f"{rows} of expert 0's {e0r} rows against its weight",
+                                          "gemm_GFLOPs": round(2.0 * rows * 2048 * 7168 / tmg / 1e9, 2)}
+            log(f"[bench] oracle per configuration: {cpu_configs}")
+
+    clk = gemm_clock_ghz() if args.workload == "large" else None
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -440,8 +644,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": gemm_traffic() if args.workload == "large" else None,
-                     "kernel": "gemm_kernel<FPROP>", "avg_us": round(tg, 2), "median_us": round(tg_med, 2)},
+                     "kernel": "gemm_kernel<FPROP>", "avg_us": round(tg, 2), "us_stats": rnd(st_tg),
+                     # the 5.0 PF peak assumes 2.4 GHz; the clock under this GEMM, from the
+                     # committed rocprofv3 counters (GRBM_GUI_ACTIVE / duration), scales it
+                     "clock_ghz": clk,
+                     "frac_at_measured_clock": (round(gemm_tflops / (PEAK_FP8_TFLOPS * clk / 2.4), 4)
+                                                if clk else None)},
         "cpu_baseline": cpu,
+        "cpu_baseline_per_config": cpu_configs,
         "breakdown": {
             "frac_of_fp8_peak_incl_quant": round(value / PEAK_FP8_TFLOPS, 4),
             "quant_act_us": round(tq_x, 2), "quant_act_GBps": round(bytes_qx / tq_x / 1e3, 1),
@@ -451,21 +661,29 @@ def main():
             "gemm_us": round(tg, 2), "gemm_TFLOPs": round(gemm_tflops, 1),
             "requant_t_us": round(t_rq, 2), "requant_t_GBps": round(bytes_rq / t_rq / 1e3, 1),
             "requant_t_frac_hbm": round(bytes_rq / t_rq / 1e3 / PEAK_HBM_GBS, 4),
-            "quant_timing": "each kernel alone after a 512 MB read (MALL evicted), HIP events, mean",
+            "quant_act_frac_ceiling": (round(ceilings["stream_2to1_X"]["us"] / tq_x, 4) if ceilings else None),
+            "quant_w_frac_ceiling": (round(ceilings["stream_2to1_W"]["us"] / tq_w, 4) if ceilings else None),
+            "quant_act_us_stats": rnd(st_tq_x), "quant_w_us_stats": rnd(st_tq_w),
+            "requant_t_us_stats": rnd(st_t_rq),
+            "quant_timing": "each kernel alone after a 512 MB read (MALL evicted), one HIP event pair per launch; "
+                            "us = mean; frac_ceiling = the plain 2:1 stream's time over the same elements / "
+                            "the quantiser's",
         },
+        "ceilings": ceilings,
+        "probes": probes,
         "other_configs": others,
         "variants": {
             "pow2_scales": {
                 "what": "the same step with power-of-two scales, applied by the scaled matrix instruction",
                 "value": round(flops / (ms_step_p2 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                "ms_per_step": round(ms_step_p2, 4), "gemm_us": round(tg_p2, 2),
+                "ms_per_step": round(ms_step_p2, 4), "gemm_us": round(tg_p2, 2), "gemm_us_stats": rnd(st_tg_p2),
                 "gemm_TFLOPs": round(flops / (tg_p2 * 1e-6) / 1e12, 1),
                 "kernel": "gemm_pow2_kernel<FPROP>",
             },
             "producer_fusion": {
                 "what": "GEMM whose epilogue writes Y as E4M3 codes + 1x128 scales (no bf16 Y), against the GEMM "
                         "writing bf16 Y followed by the 1x128 quantiser of Y",
-                "fused_us": round(t_fq, 2), "separate_us": round(t_sq, 2),
+                "fused_us": round(t_fq, 2), "separate_us": round(t_sq, 2), "fused_us_stats": rnd(st_t_fq),
                 "fused_TFLOPs": round(flops / (t_fq * 1e-6) / 1e12, 1),
                 "hbm_bytes_saved": 4 * M * N,
                 "kernel": "gemm_kernel<FPROP, QMODE=1>",
@@ -473,7 +691,7 @@ def main():
             "decode_grouped": {
                 "what": f"{dec.name}: rows per expert {[int(c) for c in dec.real_rows]} (unpadded), "
                         "bf16 out; HBM-bound (each expert's FP8 weight streamed once); timed cold",
-                "us": round(t_dec, 2), "GBps": round(bytes_dec / t_dec / 1e3, 1),
+                "us": round(t_dec, 2), "GBps": round(bytes_dec / t_dec / 1e3, 1), "us_stats": rnd(st_t_dec),
                 "roofline": {"bound": "hbm", "achieved": round(bytes_dec / t_dec / 1e3, 1), "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": round(bytes_dec / t_dec / 1e3 / PEAK_HBM_GBS, 4),
                              "traffic": None},

@@ -13,14 +13,20 @@
 //
 //  * absmax is an integer max over the bf16 magnitude bits (bits & 0x7fff
 //    order like the values for finite inputs);
-//  * the exact quotient fl32(x / s) is needed only to pick an E4M3 code. With
-//    r ~ 1 / s, rlo = fl32(r (1 - 2^-19)), rhi = fl32(r (1 + 2^-19)), the
-//    products x*rlo and x*rhi bracket fl32(x / s) strictly (see make_scale for
-//    the error budget; for x / s below fp32's normal range all three encode to
-//    a signed zero). The conversion is monotone, so when both brackets give
-//    the same code it is the code of fl32(x / s). Otherwise (about 6 elements
-//    in 10^5) the lane recomputes with the correctly-rounded division. Groups
-//    whose scale is below 2^-100 always take the division.
+//  * the exact quotient fl32(x / s) comes from one correctly rounded
+//    reciprocal per group, y = RN(1 / s), and per element q0 = RN(x y),
+//    e = RN(s q0 - x) (exact: the remainder of a quotient within an ulp),
+//    q = RN(q0 - e y): Markstein's correction, which gives RN(x / s) whenever
+//    nothing underflows. Checked on the CPU for every positive finite bf16
+//    absmax with s >= 2^-100 against every bf16 x with |x| <= absmax, both
+//    signs (1.04e9 pairs, tests/exact_quotient_check.c): the E4M3 codes are
+//    those of RN(x / s) in every case; the quotient bits differ only below
+//    2^-11, where both encode to the same signed zero. Branch-free: the
+//    earlier bracket test (two reciprocal products, exact division where they
+//    disagreed) sent a whole wave through four divisions whenever one lane's
+//    quotient lay near an E4M3 rounding midpoint, which bf16 data hits for
+//    about 0.5% of elements (ratios of short mantissas). Groups whose scale is
+//    below 2^-100 divide.
 //  * v_cvt_pk_fp8_f32 rounds to nearest even, keeps the sign of zero and handles
 //    fp32 denormals like the E4M3 definition on every finite input below 448,
 //    and returns 448 for inputs in [448, 464]. No quotient here exceeds 450
@@ -53,7 +59,7 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 }
 
 struct TileScale {
-  float s, rlo, rhi;
+  float s, y;   // the scale and its reciprocal (RN(1 / s); 2^-k for a power of two)
   bool fast;
 };
 
@@ -62,9 +68,7 @@ struct TileScale {
 //    corrected once with the exact residual amax - 448 q (an FMA), which gives
 //    the correctly rounded quotient for every bf16 amax (checked for all 32639
 //    positive finite bf16 values, on the CPU and by the GPU parity tests).
-//  * r approximates 1 / s with the hardware reciprocal (documented within 1
-//    ulp); the brackets x * r (1 -+ 2^-19) enclose fl32(x / s) strictly as
-//    long as r is within 13 ulp: e_r + 2 * 2^-24 < 2^-19 - 2^-24.
+//  * y = RN(1 / s), the IEEE division (once per group).
 __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits16) {
   TileScale t;
   const float amax = __uint_as_float(amax_bits16 << 16);
@@ -72,13 +76,13 @@ __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits16) {
   const float q = amax * c;
   t.s = __builtin_fmaf(__builtin_fmaf(-q, kFmax, amax), c, q);     // fl32(amax / 448)
   if (t.s == 0.0f) {
-    t.rlo = t.rhi = 0.0f;                  // +-0 * 0 keeps the sign of zero
+    // all-zero group: y = 0 turns every +-0 into the same-signed zero
+    // (q0 = +-0, e = +0, q = +-0), as the method's s = 0, q = +-0 rule asks
+    t.y = 0.0f;
     t.fast = true;
   } else {
     t.fast = t.s >= kFastScaleMin;
-    const float r = t.fast ? __builtin_amdgcn_rcpf(t.s) : 0.0f;
-    t.rlo = r * (1.0f - 0x1p-19f);
-    t.rhi = r * (1.0f + 0x1p-19f);
+    t.y = t.fast ? 1.0f / t.s : 0.0f;
   }
   return t;
 }
@@ -96,7 +100,7 @@ __device__ __forceinline__ TileScale make_scale_pow2(uint32_t amax_bits16) {
   const int k = max(-127, min(127, e - 135 + (m > 96 ? 1 : 0)));
   TileScale t;
   t.s = k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(0x00400000u);
-  t.rlo = t.rhi = __uint_as_float((uint32_t)(127 - k) << 23);      // 2^-k, a normal fp32 for k <= 120
+  t.y = __uint_as_float((uint32_t)(127 - k) << 23);                // 2^-k, a normal fp32 for k <= 120
   t.fast = true;
   return t;
 }
@@ -107,15 +111,22 @@ __device__ __forceinline__ TileScale group_scale(uint32_t amax_bits16) {
   else return make_scale(amax_bits16);
 }
 
-// Encodes four values (one output dword). Exact scales: the exact codes are
-// computed only when the brackets disagree. Power-of-two scales: one exact
-// product and one conversion.
+// RN(x / s) from the group's reciprocal (Markstein's correction; see above).
+// The negations are exact, so x = -0 gives -0 like the division.
+__device__ __forceinline__ float exact_quotient(float x, const TileScale& t) {
+  const float q0 = x * t.y;
+  const float e = __builtin_fmaf(t.s, q0, -x);
+  return __builtin_fmaf(-e, t.y, q0);
+}
+
+// Encodes four values (one output dword). Exact scales: the correctly rounded
+// quotients from the group's reciprocal, or the division itself for groups
+// with 0 < s < 2^-100. Power-of-two scales: one exact product.
 template <bool POW2>
 __device__ __forceinline__ uint32_t encode4(float f0, float f1, float f2, float f3, const TileScale& t) {
-  if constexpr (POW2) return cvt4(f0 * t.rlo, f1 * t.rlo, f2 * t.rlo, f3 * t.rlo);
-  const uint32_t lo = cvt4(f0 * t.rlo, f1 * t.rlo, f2 * t.rlo, f3 * t.rlo);
-  const uint32_t hi = cvt4(f0 * t.rhi, f1 * t.rhi, f2 * t.rhi, f3 * t.rhi);
-  if (__builtin_expect(t.fast && lo == hi, 1)) return lo;
+  if constexpr (POW2) return cvt4(f0 * t.y, f1 * t.y, f2 * t.y, f3 * t.y);
+  if (__builtin_expect(t.fast, 1))
+    return cvt4(exact_quotient(f0, t), exact_quotient(f1, t), exact_quotient(f2, t), exact_quotient(f3, t));
   return cvt4(f0 / t.s, f1 / t.s, f2 / t.s, f3 / t.s);
 }
 

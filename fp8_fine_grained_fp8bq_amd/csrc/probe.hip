@@ -16,6 +16,8 @@
 //    register-resident operands, with or without the promotion FMAs (four per
 //    instruction, as the exact-scale GEMM issues them), and reports the shader
 //    clock the chip holds in each case.
+//  * Memory. fp8bq_probe_stream_2to1 is the quantisers' traffic (2 bytes read,
+//    1 written per element) with no arithmetic: their measured ceiling.
 #include "../../include/fp8bq_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -165,6 +167,19 @@ __global__ __launch_bounds__(512) void stream_kernel(const uint8_t* codes, const
   }
 }
 
+// Streaming ceiling of the quantisers' traffic: read 2 bytes, write 1 byte per
+// element (lane i reads bytes [32 i, 32 i + 32) and writes the 16 high bytes of
+// its 16 bf16 to bytes [16 i, 16 i + 16)), with no arithmetic beyond a byte
+// permute: what the memory system delivers for the quantisers' read/write mix.
+__global__ __launch_bounds__(256) void stream21_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                       int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const uint4 a = src[2 * i], b = src[2 * i + 1];
+  auto hi = [](uint32_t u, uint32_t v) { return __builtin_amdgcn_perm(v, u, 0x07050301u); };
+  dst[i] = make_uint4(hi(a.x, a.y), hi(a.z, a.w), hi(b.x, b.y), hi(b.z, b.w));
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,3 +223,15 @@ int fp8bq_probe_mfma_stream(int fold, int64_t iters, int32_t workgroups, const v
 }
 
 }  // extern "C"
+
+extern "C" int fp8bq_probe_stream_2to1(const void* src, void* dst, int64_t n, void* stream) {
+  if (!src || !dst) return fail(FP8BQ_E_INVAL, "stream_2to1: null pointer");
+  if (n <= 0 || n % 16 || n / 16 / 256 >= ((int64_t)1 << 31))
+    return fail(FP8BQ_E_SHAPE, "stream_2to1: n must be a positive multiple of 16 (and below 2^43)");
+  if (((uintptr_t)src | (uintptr_t)dst) % 16) return fail(FP8BQ_E_ALIGN, "stream_2to1: src and dst must be 16-byte aligned");
+  if (int st = check_gfx950()) return st;
+  const int64_t n16 = n / 16;
+  hipLaunchKernelGGL(stream21_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, (uint4*)dst, n16);
+  return launched("stream_2to1");
+}

@@ -12,7 +12,8 @@ from . import STATUS_NAMES, Fp8bqError
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp8bq_probe.so")
-EXPORTS = ("fp8bq_probe_mfma_accum", "fp8bq_probe_mfma_once", "fp8bq_probe_mfma_stream", "fp8bq_probe_last_error")
+EXPORTS = ("fp8bq_probe_mfma_accum", "fp8bq_probe_mfma_once", "fp8bq_probe_mfma_stream", "fp8bq_probe_stream_2to1",
+           "fp8bq_probe_last_error")
 
 _lib = None
 
@@ -27,7 +28,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_probe_mfma_accum.argtypes = [vp, vp, i64, vp, vp, vp]
         L.fp8bq_probe_mfma_once.argtypes = [vp, vp, vp, vp, vp]
         L.fp8bq_probe_mfma_stream.argtypes = [i32, i64, ctypes.c_int32, vp, vp, vp, vp, vp]
-        for f in EXPORTS[:3]:
+        L.fp8bq_probe_stream_2to1.argtypes = [vp, vp, i64, vp]
+        for f in EXPORTS[:4]:
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_probe_last_error.restype = ctypes.c_char_p
         L.fp8bq_probe_last_error.argtypes = []
@@ -54,5 +56,9 @@ def fp8bq_probe_mfma_stream(fold, iters, workgroups, codes, scales, sink, ticks,
                   lib().fp8bq_probe_mfma_stream(fold, iters, workgroups, codes, scales, sink, ticks, stream))
 
 
-__all__ = ["EXPORTS", "LIB_PATH", "lib", "fp8bq_probe_mfma_accum", "fp8bq_probe_mfma_once",
+def fp8bq_probe_stream_2to1(src, dst, n, stream=0):
+    return _check("fp8bq_probe_stream_2to1", lib().fp8bq_probe_stream_2to1(src, dst, n, stream))
+
+
+__all__ = ["fp8bq_probe_stream_2to1", "EXPORTS", "LIB_PATH", "lib", "fp8bq_probe_mfma_accum", "fp8bq_probe_mfma_once",
            "fp8bq_probe_mfma_stream", "STATUS_NAMES"]

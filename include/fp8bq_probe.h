@@ -64,6 +64,15 @@ int fp8bq_probe_mfma_once(const void* a, const void* b, const float* c, float* d
 int fp8bq_probe_mfma_stream(int fold, int64_t iters, int32_t workgroups, const void* codes, const float* scales,
                             float* sink, unsigned long long* ticks, void* stream);
 
+/* Streaming ceiling of the quantisers' memory traffic: reads n bf16 (2n bytes)
+ * from src and writes n bytes to dst (the high byte of each bf16), 32 bytes read
+ * and 16 written per lane, nothing else. The quantisers move the same bytes per
+ * element (plus 4 per 128-element tile), so its rate on a cold (MALL-evicted)
+ * input is the ceiling their GB/s is compared with.
+ * src, dst  device, 16-byte aligned, not overlapping; n a multiple of 16.
+ * Errors: E_INVAL null pointer, E_SHAPE bad n, E_ALIGN, E_DEVICE, E_HIP. */
+int fp8bq_probe_stream_2to1(const void* src, void* dst, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

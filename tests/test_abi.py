@@ -293,4 +293,7 @@ def test_probe_validation(P):
     assert P.fp8bq_probe_mfma_stream(1, 0, 256, A16, S4, S4, S4, None) == fb.E_INVAL
     assert P.fp8bq_probe_mfma_stream(1, 16, 0, A16, S4, S4, S4, None) == fb.E_INVAL
     assert P.fp8bq_probe_mfma_stream(1, 16, 256, A16 + 1, S4, S4, S4, None) == fb.E_ALIGN
+    assert P.fp8bq_probe_stream_2to1(None, B16, 1024, None) == fb.E_INVAL
+    assert P.fp8bq_probe_stream_2to1(A16, B16, 1000, None) == fb.E_SHAPE
+    assert P.fp8bq_probe_stream_2to1(A16, B16 + 4, 1024, None) == fb.E_ALIGN
     assert "aligned" in P.fp8bq_probe_last_error().decode()

@@ -133,3 +133,15 @@ def test_power_stream_runs():
         torch.cuda.synchronize()
         assert bool(torch.isfinite(sink).all())
         assert bool((ticks > 0).all())
+
+
+def test_stream_2to1_moves_the_bytes():
+    import torch
+    probe = _probe()
+    n = 1 << 20
+    src = torch.randint(-32768, 32767, (n,), dtype=torch.int16, device="cuda")
+    dst = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    log("[probe] stream 2-to-1")
+    probe.fp8bq_probe_stream_2to1(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    expect = (src.cpu().numpy().view(np.uint16) >> 8).astype(np.uint8)
+    np.testing.assert_array_equal(host(dst), expect)
