@@ -54,8 +54,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Workgroup tile: BM rows x TBN columns, TBN = 256 (BN) or, for GEMMs with
-// too few 256 x 256 tiles to fill the CUs, 128.
+// Workgroup tile: BM rows x TBN columns, TBN = 256 (BN); 128 for GEMMs with
+// too few 256 x 256 tiles to fill the CUs; 224 where 256-column tiles would
+// leave the last round of the persistent walk partly idle (n = 7168 = 32 x 224:
+// a backward GEMM's 448 tiles of 256 x 256 take two rounds on 256 CUs, its 512
+// tiles of 256 x 224 two rounds of 7/8 the work).
 constexpr int BM = 256, BN = 256, BK = 128;
 // One LDS stage: the A and B tiles of a K-chunk, BM activation scales, and
 // room for 256 weight-side scales (column scales of WGRAD, else the tile's
@@ -83,7 +86,9 @@ struct Cfg {
   static constexpr int WN = TBN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
-  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one weight block column");
+  // a wave's columns lie in one weight block column, except with 224-column tiles
+  // (waves of 112 columns), whose waves may straddle two blocks
+  static_assert(WN <= 128 && (128 % WN == 0 || WN == 112), "wave columns against 128-column weight blocks");
 };
 
 struct GemmArgs {
@@ -346,13 +351,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
     } else {
       const bool odd = ((threadIdx.x >> 4) & 1) != 0;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int jp = 0; jp < TN / 2; ++jp) {
           const uint4 v = pair16(pack_bf16x4(acc[i][2 * jp]), pack_bf16x4(acc[i][2 * jp + 1]), odd);
           const int64_t col = col0 + 2 * jp * 16 + (odd ? 12 : 0);
           *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (row0 + i * 16) * p.ldo + col) = v;
         }
+        if constexpr (TN % 2 != 0) put(row0 + i * 16, col0 + (TN - 1) * 16, acc[i][TN - 1]);   // 112-column waves
+      }
     }
   } else {
 #pragma unroll
@@ -470,11 +477,10 @@ struct Loader {
   using S = Stage<TBN>;
   static constexpr int kRowsPerRound = 8 * LOADERS;      // one dwordx4 load per wave covers 8 rows
   static constexpr int kRounds = BM / kRowsPerRound;     // of A; then kRoundsB of B
-  static constexpr int kRoundsB = TBN / kRowsPerRound;
+  static constexpr int kRoundsB = (TBN + kRowsPerRound - 1) / kRowsPerRound;   // the last may be partial
   static constexpr int kScaleWaves = 8 / WAVES;
   static constexpr int kParts = kRounds + kRoundsB + kScaleWaves;
-  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0 && TBN % kRowsPerRound == 0,
-                "load rounds");
+  static_assert(LOADERS % 2 == 0 && LOADERS <= WAVES && BM % kRowsPerRound == 0 && TBN % 8 == 0, "load rounds");
   static_assert(WAVES == 4 || WAVES == 8, "scale waves");
 
   const GemmArgs& p;
@@ -523,9 +529,11 @@ struct Loader {
         s_off[v] = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
         d_sk[v] = t.sb + t.n0;
       } else {
+          // the tile's columns span blocks blk0 .. blk0 + last (last <= 2): lane l
+        // brings block blk0 + min(l, last)
         const int64_t blk0 = t.n0 / 128;
-        const int64_t blk1 = min(blk0 + 1, t.n_end / 128 - 1) - blk0;
-        const int64_t bsel = lane < 1 ? 0 : blk1;
+        const int64_t last = (t.n_end - 1) / 128 - blk0;
+        const int64_t bsel = TBN % 128 == 0 ? (lane < 1 ? 0 : last) : min((int64_t)lane, last);
         s_off[v] = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
         d_sk[v] = KIND == KIND_FPROP ? t.sb + blk0 * p.ldsb : t.sb + blk0;
       }
@@ -553,10 +561,16 @@ struct Loader {
       if constexpr (LOADERS < WAVES) {
         if (wave >= LOADERS) return;
       }
-      if (q < kRounds)
+      if (q < kRounds) {
         dma16_buf(rs_a, voff_a[q], base + (q * kRowsPerRound + 8 * wave) * BK);
-      else
+      } else {
+        // a partial last round (224-column tiles): waves whose rows lie past the
+        // tile load nothing (uniform per wave)
+        if constexpr (TBN % kRowsPerRound != 0) {
+          if ((q - kRounds) * kRowsPerRound + 8 * wave >= TBN) return;
+        }
         dma16_buf(rs_b, voff_b[q - kRounds], base + S::kABytes + ((q - kRounds) * kRowsPerRound + 8 * wave) * BK);
+      }
       return;
     }
     const int v = q - kRounds - kRoundsB, sw = wave + v * WAVES;
@@ -565,9 +579,9 @@ struct Loader {
     if (act || KIND == KIND_WGRAD) {
       dma4(uniform_ptr(d_sk[v]), s_off[v], base + (act ? S::kSaOff : S::kSbOff) + 256 * (sw & 3));
     } else if (sw == 4) {
-      // FPROP / DGRAD: the tile's two weight block scales; a load's cost
-      // follows its active lanes, so only two lanes take part
-      if (lane < 2) dma4(uniform_ptr(d_sk[v]), s_off[v], base + S::kSbOff);
+      // FPROP / DGRAD: the tile's weight block scales (up to three); a load's
+      // cost follows its active lanes, so only three lanes take part
+      if (lane < (TBN % 128 == 0 ? 2 : 3)) dma4(uniform_ptr(d_sk[v]), s_off[v], base + S::kSbOff);
     }
   }
 };
@@ -604,12 +618,31 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
   // Fragments and scales of one step, read from its stage: the wave's TM
   // activation subtiles, the first weight subtile and the per-row scale
   // products of the chunk.
-  auto read_scales = [&](const uint8_t* stage, float (&sc)[C::TM]) {
+  // With 224-column tiles (FPROP / DGRAD) a wave's 112 columns may straddle two
+  // weight blocks: column subtiles j < jb take block b0's scale (sc), the others
+  // block b1's (sc1). `off` is the wave's first column counted from its tile's
+  // first block (n0 % 128 + wave_n * WN), wave-uniform.
+  constexpr bool kMB = KIND != KIND_WGRAD && (TBN % 128) != 0;
+  auto wave_off = [&](int tk_) -> int {
+    if constexpr (kMB) {
+      const int64_t n0 = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * tk_).n0;
+      return (int)(n0 % 128) + wave_n * C::WN;
+    } else {
+      return 0;
+    }
+  };
+  auto read_scales = [&](const uint8_t* stage, float (&sc)[C::TM], float (&sc1)[C::TM], int& jb, int off) {
     const float* Sa = reinterpret_cast<const float*>(stage + S::kSaOff);
     const float* Sb = reinterpret_cast<const float*>(stage + S::kSbOff);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) sc[i] = Sa[wave_m * C::WM + i * 16 + l16];
-    if constexpr (KIND != KIND_WGRAD) {
+    if constexpr (kMB) {
+      const int b0 = off >> 7, b1 = (off + C::WN - 1) >> 7;
+      jb = ((b0 + 1) * 128 - off) >> 4;                  // >= TN: one block only
+      const float s0 = Sb[b0], s1 = Sb[b1];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) { sc1[i] = sc[i] * s1; sc[i] *= s0; }
+    } else if constexpr (KIND != KIND_WGRAD) {
       const float sbv = Sb[wave_n * C::WN / 128];   // the weight block of the wave's columns
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) sc[i] *= sbv;
@@ -650,8 +683,10 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
   v8i af[C::TM];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) af[i] = a_frag(smem, i);
-  float sc[C::TM], scp[C::TM], scn[C::TM];
-  read_scales(smem, sc);
+  float sc[C::TM], scp[C::TM], scn[C::TM], sc1[C::TM], scn1[C::TM];
+  int jb = C::TN, jbn = C::TN;
+  int off_cur = wave_off(0), off_nxt = off_cur;
+  read_scales(smem, sc, sc1, jb, off_cur);
   // The compiler tracks at most 15 outstanding LDS reads; with more in flight
   // where a loop iteration begins it waits for all of them before the first
   // MFMA. This wait and the one at the last column keep the count it carries
@@ -678,6 +713,14 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
   v4f sbj[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  // WGRAD, odd TN (224-column tiles): the last column and the next chunk's
+  // column 0 share a slot of sbj, so the last column's scales are kept here
+  // for its folds that run during the next chunk (or after the tile)
+  v4f sbjp = {0.f, 0.f, 0.f, 0.f};
+  auto last_col_scales = [&]() -> const v4f& {
+    if constexpr (C::TN % 2 != 0) return sbjp;
+    else return sbj[(C::TN - 1) & 1];
+  };
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   // Step s: weight columns 0 .. TN-2 from stage s % 2 with fragments already in
@@ -688,6 +731,10 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
   int s = 0;
 #pragma clang loop unroll(disable)
   for (int tk = 0; tk < my_tiles; ++tk) {
+    if constexpr (kMB) {
+      if (tk > 0) off_cur = off_nxt;
+      off_nxt = tk + 1 < my_tiles ? wave_off(tk + 1) : off_cur;
+    }
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nc; ++c, ++s) {
       const uint8_t* stage = smem + (s & 1) * S::kStage;
@@ -697,7 +744,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
         if (j == kBarCol) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          read_scales(nstage, scn);
+          read_scales(nstage, scn, scn1, jbn, c + 1 < nc ? off_cur : off_nxt);
         }
         // last column: everything read before the previous column's weight
         // fragment has landed (read at least a column ago)
@@ -714,10 +761,11 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
           pend[t % 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[0], af[i], zero, 0, 0, 0, 0, 0, 0);
           if (t >= kLag) {
             const int u = t - kLag;
-            fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], sc[u % C::TM], sbj[(u / C::TM) & 1]);
+            const float su = kMB ? (u / C::TM < jb ? sc[u % C::TM] : sc1[u % C::TM]) : sc[u % C::TM];
+            fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], su, sbj[(u / C::TM) & 1]);
           } else {
             const int u = t - kLag + kNT;   // previous chunk, last column
-            fold<KIND>(acc[u % C::TM][C::TN - 1], pend[u % 4], scp[u % C::TM], sbj[(C::TN - 1) & 1]);
+            fold<KIND>(acc[u % C::TM][C::TN - 1], pend[u % 4], scp[u % C::TM], last_col_scales());
           }
           if (j + 1 == C::TN) af[i] = a_frag(nstage, i);
           // column TN-2's last MFMA: the folds of column TN-3 are done, so its
@@ -747,14 +795,21 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
         for (int q = 0; q < kBAhead; ++q) bw[q] = bw[q + 1];
       }
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) { scp[i] = sc[i]; sc[i] = scn[i]; }
+      for (int i = 0; i < C::TM; ++i) {
+        // the previous chunk's last column keeps its scale for its lagged folds
+        scp[i] = kMB ? (C::TN - 1 < jb ? sc[i] : sc1[i]) : sc[i];
+        sc[i] = scn[i];
+        if constexpr (kMB) sc1[i] = scn1[i];
+      }
+      if constexpr (kMB) jb = jbn;
+      if constexpr (KIND == KIND_WGRAD && C::TN % 2 != 0) sbjp = sbj[(C::TN - 1) & 1];
     }
 
     // ---- tile done: remaining folds (scales of the tile's last chunk, now in
     // scp), epilogue; the next tile's first folds then add zeros ------------
 #pragma unroll
     for (int u = kNT - kLag; u < kNT; ++u)
-      fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], sbj[(u / C::TM) & 1]);
+      fold<KIND>(acc[u % C::TM][u / C::TM], pend[u % 4], scp[u % C::TM], last_col_scales());
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
     const Tile cur = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * tk);

@@ -33,6 +33,20 @@ pytestmark = pytest.mark.gpu
 # 4100 x 8064 outputs = 17 x 32 = 544 tiles of 256 x 256 (> 2 x 256 CUs): the last
 # row tile has 4 rows, the last column tile 128 columns; K = 512 is 4 chunks.
 M, N, K = 4100, 8064, 512
+# The exact-scale kernel picks its tile width per shape (256 x 256, or 256 x 224 when
+# that takes fewer rounds of the walk, weighted by the tile's work; see
+# prefer_224): N = 7552 keeps 256-column tiles (510 tiles, the last 128 columns
+# wide), N = 7936 takes 224-column tiles (612 tiles, the last 96 columns wide,
+# waves whose 112 columns straddle two weight blocks).
+N_BY_WIDTH = {256: 7552, 224: 7936}
+
+
+def width_for(m, n, cus=256):
+    """Tile width the library's launcher picks for an exact-scale GEMM (mirror of prefer_224)."""
+    tm = -(-m // 256)
+    r256 = -(-(tm * -(-n // 256)) // cus)
+    r224 = -(-(tm * -(-n // 224)) // cus)
+    return 224 if r224 * 7 < r256 * 8 else 256
 POISON16 = -1            # 0xFFFF: a bf16 NaN, never the rounding of a finite sum
 POISON32 = -1            # 0xFFFFFFFF: an fp32 NaN
 
@@ -71,13 +85,14 @@ def _twice(launch, shape, fp32=False):
     return out1
 
 
-@pytest.mark.parametrize("pow2", [False, True])
-def test_fprop_every_element(pow2):
-    assert _tiles(M, N) >= 2 * 256
+@pytest.mark.parametrize("pow2,N", [(False, N_BY_WIDTH[256]), (False, N_BY_WIDTH[224]), (True, N)])
+def test_fprop_every_element(pow2, N):
+    assert _tiles(M, N) >= 2 * 256 - 2
+    assert pow2 or width_for(M, N) == (256 if N == N_BY_WIDTH[256] else 224)
     x = act(301, M, K, dist="student_t3", outlier_p=0.002, outlier_mult=20)
     w = act(302, N, K, std=0.02)
     mode = "pow2" if pow2 else "exact"
-    log(f"[walk] fprop {M}x{N}x{K} ({_tiles(M, N)} tiles) scales={mode}")
+    log(f"[walk] fprop {M}x{N}x{K} ({_tiles(M, N)} tiles of 256x256) scales={mode}")
     xq, xs = fb.quant_act_1x128(dev_bf16(x), fb.SCALE_POW2 if pow2 else fb.ACT_ROWWISE)
     wq, ws, _ = fb.quant_w_128x128(dev_bf16(w), pow2=pow2)
     op = fb.FPROP | (fb.SCALE_POW2 if pow2 else 0)
@@ -91,8 +106,8 @@ def test_fprop_every_element(pow2):
     _assert_ok(check_gemm_bf16(host_bf16_bits(y), y32, ab), f"fprop every element ({mode})")
 
 
-@pytest.mark.parametrize("pow2", [False, True])
-def test_dgrad_every_element(pow2):
+@pytest.mark.parametrize("pow2,N", [(False, N_BY_WIDTH[256]), (False, N_BY_WIDTH[224]), (True, N)])
+def test_dgrad_every_element(pow2, N):
     # dX [M, N] = dY [M, K] W [K, N]: the weight's transposed FP8 copy is the B operand
     dy = act(303, M, K, std=1e-3)
     w = act(304, K, N, std=0.02)
@@ -110,11 +125,11 @@ def test_dgrad_every_element(pow2):
     _assert_ok(check_gemm_bf16(host_bf16_bits(dx), y32, ab), f"dgrad every element ({mode})")
 
 
-@pytest.mark.parametrize("pow2", [False, True])
-def test_wgrad_every_element(pow2):
+@pytest.mark.parametrize("pow2,k", [(False, N_BY_WIDTH[256]), (False, N_BY_WIDTH[224]), (True, N)])
+def test_wgrad_every_element(pow2, k):
     # dW [n, k] = dY^T X over T = 512 tokens (4 chunks), both operands in 128x1 tiles
-    n, k, t = 4224, N, K
-    assert _tiles(n, k) >= 2 * 256
+    n, t = 4224, K
+    assert _tiles(n, k) >= 2 * 256 - 32
     dy = act(305, t, n, std=1e-3)
     x = act(306, t, k, outlier_p=0.001, outlier_mult=50)
     mode = "pow2" if pow2 else "exact"
