@@ -52,6 +52,13 @@ int check_device() {
   return FP8BQ_OK;
 }
 
+// a * b >= limit for a, b >= 1, without forming the product (callers pass
+// user-supplied sizes, whose product may not fit in int64)
+bool product_at_least(int64_t a, int64_t b, int64_t limit) { return a > (limit - 1) / b; }
+
+// ceil(a / d) for a >= 1 without overflowing a + d - 1
+int64_t ceil_div(int64_t a, int64_t d) { return (a - 1) / d + 1; }
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FP8BQ_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return FP8BQ_OK;
@@ -80,7 +87,8 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
   if (mode == FP8BQ_ACT_ROWWISE) {
     if (ldq < cols) return fail(FP8BQ_E_INVAL, "quant_act: ldq < cols");
     if (lds < rows) return fail(FP8BQ_E_INVAL, "quant_act: lds < rows");
-    if (rows >= kMaxTiles || (rows + 31) / 32 * (cols / 128) >= kMaxTiles) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
+    if (rows >= kMaxTiles || product_at_least(ceil_div(rows, 32), cols / 128, kMaxTiles))
+      return fail(FP8BQ_E_SHAPE, "quant_act: too large");
   } else {
     if (rows % 128) return fail(FP8BQ_E_SHAPE, "quant_act: column-wise mode needs rows (%lld) to be a multiple of 128", (long long)rows);
     if (ldq < rows) return fail(FP8BQ_E_INVAL, "quant_act: ldq < rows (transposed output)");
@@ -149,12 +157,12 @@ int check_gemm_common(const char* who, int64_t m, int64_t n, int64_t k, const vo
   if (lda < k || ldb < k) return fail(FP8BQ_E_INVAL, "%s: lda and ldb must be >= k", who);
   if (ldo < n) return fail(FP8BQ_E_INVAL, "%s: ldo must be >= n", who);
   if (k % 128 || n % 128) return fail(FP8BQ_E_SHAPE, "%s: k (%lld) and n (%lld) must be multiples of 128", who, (long long)k, (long long)n);
-  if (((m + 255) / 256) * ((n + 255) / 256) >= kMaxTiles) return fail(FP8BQ_E_SHAPE, "%s: too many tiles", who);
+  if (product_at_least(ceil_div(m, 256), ceil_div(n, 128), kMaxTiles)) return fail(FP8BQ_E_SHAPE, "%s: too many tiles", who);
   if (lda >= ((int64_t)1 << 23) || ldb >= ((int64_t)1 << 23))
     return fail(FP8BQ_E_SHAPE, "%s: lda and ldb must be below 2^23 (256 rows within 2 GiB)", who);
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(sa, 4) || !aligned(sb, 4))
     return fail(FP8BQ_E_ALIGN, "%s: a, b, out must be 16-byte aligned, scales 4-byte aligned", who);
-  if (lda % 16 || ldb % 16 || (ldo * out_elem_bytes) % 16)
+  if (lda % 16 || ldb % 16 || ((ldo % 16) * out_elem_bytes) % 16)
     return fail(FP8BQ_E_ALIGN, "%s: lda, ldb must be multiples of 16 and ldo*sizeof(out) of 16 bytes", who);
   return FP8BQ_OK;
 }
@@ -257,7 +265,7 @@ int fp8bq_grouped_gemm_decode(int32_t groups, const int64_t* row_off, int64_t n,
   const int64_t m = row_off[groups];
   if (int st = check_gemm_common("grouped_gemm_decode", m > 0 ? m : 1, n, k, a, lda, sa, b, ldb, sb, out, ldo, 2))
     return st;
-  if ((int64_t)groups * (n / 64) >= ((int64_t)1 << 31)) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: too many column slices");
+  if (product_at_least(groups, n / 64, (int64_t)1 << 31)) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: too many column slices");
   if (ldsa < m) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsa must be >= m");
   if (ldsb < k / 128) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsb must be >= k / 128");
   if (int st = check_device()) return st;

@@ -44,7 +44,7 @@ constexpr int kDN = 64;   // output columns per workgroup
 
 // LDS DMA of one dword per lane through a raw buffer resource (see dma16_buf).
 __device__ __forceinline__ void dma4_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
 }
 

@@ -119,13 +119,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 // M0 is reserved by the compiler; on gfx950 only LDS DMA reads it and the
 // compiler itself never keeps a value there across these statements (the
-// build passes -Wno-inline-asm for this clobber).
+// build passes -Wno-inline-asm for this clobber). An SALU write of M0 needs
+// one wait state before an LDS DMA reads it (the compiler puts an s_nop 0
+// there for its own LDS-DMA builtins; its hazard check cannot see inside an
+// asm block, so each block carries the s_nop itself). tests/test_lds_dma_m0.py
+// checks the built code objects: every M0 use is this write, wait, DMA triple.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 // The same 16-byte LDS DMA through a raw buffer resource (base, byte bound):
@@ -133,7 +137,7 @@ __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t 
 // or past the bound reads nothing from memory and its bytes come back as
 // zeros.
 __device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
 }
 // Raw buffer resource over [base, end) (bound capped at 4 GiB - 1: offsets

@@ -1,0 +1,221 @@
+// Host-only driver for the C ABI layer (fp8_fine_grained_fp8bq_amd/csrc/api.cpp)
+// built with AddressSanitizer and UndefinedBehaviorSanitizer (g++, no GPU
+// code): it runs the argument-validation paths of every entry point, and the
+// accepted calls through to stand-ins for the kernel launchers, against stub
+// HIP device queries that report either no device or one gfx950. Any memory
+// error or undefined behaviour (an overflowing size product, an out-of-range
+// shift, a bad read of the group offsets) aborts the run with the sanitizer's
+// report. Built and run by tests/test_abi_sanitized.py.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "fp8bq.h"
+
+// ---- stand-ins for the HIP device queries the ABI layer makes ----------------
+static bool g_have_device = false;
+static int g_launches = 0;
+
+extern "C" hipError_t hipGetDevice(int* d) {
+  if (!g_have_device) return hipErrorNoDevice;
+  *d = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipGetDevicePropertiesR0600(hipDeviceProp_tR0600* p, int) {
+  std::memset(p, 0, sizeof(*p));
+  std::strcpy(p->gcnArchName, "gfx950:sramecc+:xnack-");
+  return hipSuccess;
+}
+extern "C" hipError_t hipGetLastError(void) { return hipSuccess; }
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+
+// ---- stand-ins for the launchers: record the call, check what reached them ----
+namespace fp8bq {
+#define LAUNCHED() (++g_launches, hipSuccess)
+hipError_t launch_quant_act_rows(const uint16_t*, int64_t rows, int64_t cols, int64_t, uint8_t*, int64_t, float*,
+                                 int64_t lds, bool, hipStream_t) {
+  if (rows <= 0 || cols % 128 || lds < rows) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_quant_act_cols(const uint16_t*, int64_t rows, int64_t cols, int64_t, uint8_t*, int64_t, float*,
+                                 int64_t, bool, hipStream_t) {
+  if (rows % 128 || cols % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_quant_w(const uint16_t*, int64_t n, int64_t k, int64_t, uint8_t*, int64_t, float*, int64_t,
+                          uint8_t*, int64_t, bool, hipStream_t) {
+  if (n % 128 || k % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_requant_t(const uint8_t*, int64_t rows, int64_t cols, int64_t, const float*, int64_t, uint8_t*,
+                            int64_t, float*, int64_t, hipStream_t) {
+  if (rows % 128 || cols % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_gemm(int kind, int64_t, int64_t n, int64_t k, const uint8_t*, int64_t, const float*, int64_t,
+                       const uint8_t*, int64_t, const float*, int64_t, void*, int64_t, bool, hipStream_t) {
+  if (kind < 0 || kind > 2 || n % 128 || k % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_gemm_quant(int kind, int64_t, int64_t n, int64_t k, const uint8_t*, int64_t, const float*,
+                             int64_t, const uint8_t*, int64_t, const float*, int64_t, uint16_t*, int64_t, uint8_t*,
+                             int64_t, float*, int64_t, bool, bool, hipStream_t) {
+  if (kind < 0 || kind > 1 || n % 128 || k % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t, int64_t, const uint8_t*, int64_t,
+                               const float*, int64_t, const uint8_t*, int64_t, const float*, int64_t, uint16_t*,
+                               int64_t, bool, hipStream_t) {
+  for (int e = 0; e < groups; ++e)
+    if (row_off[e + 1] < row_off[e] || row_off[e] % 128) std::abort();
+  return LAUNCHED();
+}
+hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t, int64_t, const uint8_t*,
+                                      int64_t, const float*, int64_t, const uint8_t*, int64_t, const float*,
+                                      int64_t, uint16_t*, int64_t, hipStream_t) {
+  for (int e = 0; e < groups; ++e)
+    if (row_off[e + 1] < row_off[e] || row_off[e + 1] - row_off[e] > 256) std::abort();
+  return LAUNCHED();
+}
+}  // namespace fp8bq
+
+// ---- the checks ----------------------------------------------------------------
+static int g_fail = 0;
+#define EXPECT(call, want)                                                                              \
+  do {                                                                                                  \
+    const int got_ = (call);                                                                            \
+    if (got_ != (want)) {                                                                               \
+      std::printf("line %d: %s returned %d, expected %d (%s)\n", __LINE__, #call, got_, (want),        \
+                  fp8bq_last_error());                                                                  \
+      ++g_fail;                                                                                         \
+    }                                                                                                   \
+    if (got_ != FP8BQ_OK && std::strlen(fp8bq_last_error()) == 0) {                                     \
+      std::printf("line %d: empty error message\n", __LINE__);                                          \
+      ++g_fail;                                                                                         \
+    }                                                                                                   \
+  } while (0)
+
+// stand-in device addresses: aligned, never dereferenced by the ABI layer
+static void* P(uintptr_t a) { return reinterpret_cast<void*>(a); }
+static float* F(uintptr_t a) { return reinterpret_cast<float*>(a); }
+static const uintptr_t A16 = 0x10000, B16 = 0x20000, S4 = 0x30000, O16 = 0x40000, Q16 = 0x50000;
+
+static void validation() {
+  // fp8bq_quant_act_1x128
+  EXPECT(fp8bq_quant_act_1x128(nullptr, 256, 1024, 1024, 0, P(B16), 1024, F(S4), 256, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 0, 1024, 1024, 0, P(B16), 1024, F(S4), 256, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1024, 2, P(B16), 1024, F(S4), 256, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1000, 0, P(B16), 1024, F(S4), 256, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1000, 1000, 0, P(B16), 1000, F(S4), 256, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16 + 2), 256, 1024, 1024, 0, P(B16), 1024, F(S4), 256, nullptr), FP8BQ_E_ALIGN);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), (int64_t)1 << 30, 8192, 8192, 0, P(B16), 8192, F(S4), (int64_t)1 << 30,
+                               nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), INT64_MAX / 2, 1 << 20, 1 << 20, 0, P(B16), 1 << 20, F(S4), INT64_MAX / 2,
+                               nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 200, 1024, 1024, 1, P(B16), 256, F(S4), 1024, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1024, 1, P(B16), 200, F(S4), 1024, nullptr), FP8BQ_E_INVAL);
+  // fp8bq_quant_w_128x128
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 0, 384, 384, P(B16), 384, F(S4), 3, P(O16), 256, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 200, 384, 384, P(B16), 384, F(S4), 3, P(O16), 256, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 2, P(O16), 256, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 3, P(O16), 128, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 3, P(O16 + 1), 256, 0, nullptr), FP8BQ_E_ALIGN);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 3, P(O16), 256, 0x20, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), INT64_MAX - 127, INT64_MAX - 127, INT64_MAX - 127, P(B16), INT64_MAX - 127,
+                               F(S4), INT64_MAX, nullptr, 0, 0, nullptr), FP8BQ_E_SHAPE);
+  // fp8bq_requant_t_128x1
+  EXPECT(fp8bq_requant_t_128x1(nullptr, 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 200, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 256, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 384, F(S4 + 2), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_ALIGN);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 128, 128 * 65536, 128 * 65536, F(S4), 128, P(B16), 128, F(S4 + 4096),
+                               128 * 65536, 0, nullptr), FP8BQ_E_SHAPE);
+  // fp8bq_gemm, every op
+  for (int op = 0; op < 3; ++op) {
+    const int64_t ldsb = op == 0 ? 8 : op == 1 ? 3 : 384;
+    EXPECT(fp8bq_gemm(3, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, nullptr, 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1000, P(A16), 1008, F(S4), 300, P(B16), 1008, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_gemm(op, 300, 200, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 208, nullptr), FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1024, F(S4), 299, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb - 1, P(O16), 384, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1032, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_ALIGN);
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 383, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op | 0x20, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_gemm(op, INT64_MAX / 4, 1 << 20, 1 << 20, P(A16), 1 << 20, F(S4), INT64_MAX / 4, P(B16), 1 << 20,
+                      F(S4), (int64_t)1 << 22, P(O16), 1 << 20, nullptr), FP8BQ_E_SHAPE);
+  }
+  // fp8bq_gemm_quant
+  EXPECT(fp8bq_gemm_quant(2, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), 384, P(O16), 384, P(Q16),
+                          384, F(S4), 300, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_gemm_quant(0, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), 8, P(O16), 384, nullptr,
+                          384, F(S4), 300, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_gemm_quant(0, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), 8, P(O16), 384, P(Q16),
+                          368, F(S4), 300, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_gemm_quant(0, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), 8, P(O16), 384, P(Q16 + 4),
+                          384, F(S4), 300, 0, nullptr), FP8BQ_E_ALIGN);
+  // grouped
+  const int64_t off_ok[3] = {0, 256, 512}, off_neg[3] = {0, 256, 128}, off_odd[3] = {0, 100, 512};
+  EXPECT(fp8bq_grouped_gemm(0, off_ok, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_grouped_gemm(2, nullptr, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_INVAL);
+  EXPECT(fp8bq_grouped_gemm(2, off_neg, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_grouped_gemm(2, off_odd, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_grouped_gemm(2, off_ok, 2048, 7168, P(A16), 7168, F(S4), 500, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_INVAL);
+  const int64_t doff_ok[3] = {0, 30, 50}, doff_big[3] = {0, 257, 300};
+  EXPECT(fp8bq_grouped_gemm_decode(2, doff_big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, 2000, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2000, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, 2048, 7168, P(A16 + 8), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_ALIGN);
+  // sizes whose products do not fit in 64 bits
+  const int64_t huge = INT64_MAX - 127;
+  EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, huge / 128 * 128, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168,
+                                   F(S4), 56, P(O16), INT64_MAX / 64 * 64, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_grouped_gemm(2, off_ok, huge / 128 * 128, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56,
+                            P(O16), INT64_MAX / 64 * 64, 0, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), huge, huge / 128 * 128, huge / 128 * 128, 0, P(B16), huge / 128 * 128, F(S4),
+                               huge, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), huge / 128 * 128, huge / 128 * 128, huge / 128 * 128, 1, P(B16),
+                               huge / 128 * 128, F(S4), huge / 128 * 128, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_gemm(0, huge, huge / 128 * 128, huge / 128 * 128, P(A16), huge / 128 * 128, F(S4), huge, P(B16),
+                    huge / 128 * 128, F(S4), INT64_MAX, P(O16), INT64_MAX / 64 * 64, nullptr), FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_gemm_quant(0, huge, huge / 128 * 128, 1024, P(A16), 1024, F(S4), huge, P(B16), 1024, F(S4), INT64_MAX,
+                          P(O16), INT64_MAX / 64 * 64, P(Q16), INT64_MAX / 64 * 64, F(S4), huge, 0, nullptr), FP8BQ_E_SHAPE);
+}
+
+// calls that pass validation: E_DEVICE without a device, OK through the launchers with one
+static void accepted(int want) {
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1024, 0, P(B16), 1024, F(S4), 256, nullptr), want);
+  EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1024, 1 | FP8BQ_SCALE_POW2, P(B16), 256, F(S4), 1024, nullptr), want);
+  EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 3, nullptr, 0, 0, nullptr), want);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), want);
+  for (int op = 0; op < 3; ++op) {
+    const int64_t ldsb = op == 0 ? 8 : op == 1 ? 3 : 384;
+    EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), want);
+    EXPECT(fp8bq_gemm(op | FP8BQ_SCALE_POW2, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb,
+                      P(O16), 384, nullptr), want);
+  }
+  EXPECT(fp8bq_gemm_quant(1, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), 3, nullptr, 384, P(Q16),
+                          384, F(S4), 300, FP8BQ_SCALE_POW2, nullptr), want);
+  int64_t off[257];
+  for (int e = 0; e <= 256; ++e) off[e] = 128 * (int64_t)e;
+  EXPECT(fp8bq_grouped_gemm(256, off, 2048, 7168, P(A16), 7168, F(S4), 32768, P(B16), 7168, F(S4), 56, P(O16), 2048,
+                            0, nullptr), want);
+  int64_t doff[257];
+  for (int e = 0; e <= 256; ++e) doff[e] = 7 * (int64_t)e;
+  EXPECT(fp8bq_grouped_gemm_decode(256, doff, 2048, 7168, P(A16), 7168, F(S4), 1792, P(B16), 7168, F(S4), 56,
+                                   P(O16), 2048, 0, nullptr), want);
+}
+
+int main() {
+  validation();
+  g_have_device = false;
+  accepted(FP8BQ_E_DEVICE);
+  const int before = g_launches;
+  g_have_device = true;
+  accepted(FP8BQ_OK);
+  validation();   // again, past the cached device check
+  std::printf("abi_sanitize: %d failed checks, %d launches reached\n", g_fail, g_launches - before);
+  return g_fail != 0 || g_launches == before;
+}
