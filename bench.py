@@ -58,6 +58,10 @@ def parse():
                     help="skip timing the dense, backward and MoE configurations' kernels")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample: rows of X")
     ap.add_argument("--cpu-wrows", type=int, default=8192, help="oracle sample: rows of W")
+    ap.add_argument("--leg", choices=LEGS, default=None,
+                    help="only launch one kernel of the bench (after one untimed launch) --leg-reps times: "
+                         "the command the counter summaries under profiles/ are taken with")
+    ap.add_argument("--leg-reps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -78,6 +82,170 @@ def calibrate_copy():
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+# kernels that --leg launches alone (each on the workload the bench times it on)
+LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "mfma_stream")
+
+
+def run_leg(args):
+    """Launch one kernel of the bench on its workload: one untimed launch, then
+    --leg-reps launches, each timed by HIP events on its stream (the quantisers
+    and the decode GEMM after a 512 MB read that evicts the MALL, as in the full
+    bench), after about 300 ms of untimed launches that bring the clock to its
+    sustained-load value. Under rocprofv3 the named kernel's dispatches are the
+    last --leg-reps of its name; the operands' own quantisation runs first."""
+    import torch
+
+    import fp8_fine_grained_fp8bq_amd as fb
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(0)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    leg = args.leg
+    cold = leg in ("quant_x", "quant_w", "qcol", "decode")
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
+    flops = nbytes = None
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    if leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
+        cfg = workloads.large_fprop()
+        _, M, N, K = WORKLOADS["large"]
+        x, w = dev16(cfg.x), dev16(cfg.w)
+        fl = fb.SCALE_POW2 if leg == "fprop_pow2" else 0
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+
+        def qx():
+            fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | fl, xq.data_ptr(), K, xs.data_ptr(), M, sp)
+
+        def qw():
+            fb.fp8bq_quant_w_128x128(w.data_ptr(), N, K, K, wq.data_ptr(), K, ws.data_ptr(), K // 128, None, N, fl, sp)
+
+        def gemm():
+            fb.fp8bq_gemm(fb.FPROP | fl, M, N, K, xq.data_ptr(), K, xs.data_ptr(), M, wq.data_ptr(), K,
+                          ws.data_ptr(), K // 128, y.data_ptr(), N, sp)
+
+        if leg == "quant_x":
+            fn, nbytes = qx, M * K * 3 + (K // 128) * M * 4
+        elif leg == "quant_w":
+            fn, nbytes = qw, N * K * 3 + (N // 128) * (K // 128) * 4
+        else:
+            qx()
+            qw()
+            fn, flops = gemm, 2.0 * M * N * K
+    elif leg in ("dense", "dgrad", "wgrad", "qcol"):
+        dn = workloads.dense_fprop()
+        o_x, o_w = dev16(dn.x), dev16(dn.w)
+        Md, Nd, Kd = dn.x.shape[0], dn.w.shape[0], dn.x.shape[1]
+        flops = 2.0 * Md * Nd * Kd
+        if leg == "dense":
+            o_xq, o_xs = fb.quant_act_1x128(o_x)
+            o_wq, o_ws, _ = fb.quant_w_128x128(o_w)
+            o_y = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+
+            def fn():
+                fb.fp8bq_gemm(fb.FPROP, Md, Nd, Kd, o_xq.data_ptr(), Kd, o_xs.data_ptr(), Md, o_wq.data_ptr(), Kd,
+                              o_ws.data_ptr(), Kd // 128, o_y.data_ptr(), Nd, sp)
+        elif leg == "dgrad":
+            o_dy = dev16(workloads.backward_dy())
+            o_wq, o_ws, o_wqt = fb.quant_w_128x128(o_w, transposed_copy=True)
+            o_dq, o_ds = fb.quant_act_1x128(o_dy)
+            o_dx = torch.empty((Md, Kd), dtype=torch.bfloat16, device=dev)
+
+            def fn():
+                fb.fp8bq_gemm(fb.DGRAD, Md, Kd, Nd, o_dq.data_ptr(), Nd, o_ds.data_ptr(), Md, o_wqt.data_ptr(), Nd,
+                              o_ws.data_ptr(), Kd // 128, o_dx.data_ptr(), Kd, sp)
+        else:
+            o_xqt = torch.empty((Kd, Md), dtype=torch.uint8, device=dev)
+            o_xst = torch.empty((Md // 128, Kd), dtype=torch.float32, device=dev)
+
+            def qcol_x():
+                fb.fp8bq_quant_act_1x128(o_x.data_ptr(), Md, Kd, Kd, fb.ACT_COLWISE, o_xqt.data_ptr(), Md,
+                                         o_xst.data_ptr(), Kd, sp)
+            if leg == "qcol":
+                fn, flops, nbytes = qcol_x, None, Md * Kd * 3 + (Md // 128) * Kd * 4
+            else:
+                o_dy = dev16(workloads.backward_dy())
+                o_dqt = torch.empty((Nd, Md), dtype=torch.uint8, device=dev)
+                o_dst = torch.empty((Md // 128, Nd), dtype=torch.float32, device=dev)
+                fb.fp8bq_quant_act_1x128(o_dy.data_ptr(), Md, Nd, Nd, fb.ACT_COLWISE, o_dqt.data_ptr(), Md,
+                                         o_dst.data_ptr(), Nd, sp)
+                qcol_x()
+                o_dw = torch.empty((Nd, Kd), dtype=torch.float32, device=dev)
+
+                def fn():
+                    fb.fp8bq_gemm(fb.WGRAD, Nd, Kd, Md, o_dqt.data_ptr(), Md, o_dst.data_ptr(), Nd, o_xqt.data_ptr(),
+                                  Md, o_xst.data_ptr(), Kd, o_dw.data_ptr(), Kd, sp)
+    elif leg == "decode":
+        dec = workloads.moe_decode()
+        G_d, N_d, K_d = dec.w.shape
+        m_d = int(dec.row_off[-1])
+        d_xq, d_xs = fb.quant_act_1x128(dev16(dec.x))
+        d_wq = torch.empty((G_d, N_d, K_d), dtype=torch.uint8, device=dev)
+        d_ws = torch.empty((G_d, N_d // 128, K_d // 128), dtype=torch.float32, device=dev)
+        for e in range(G_d):
+            q_e, s_e, _ = fb.quant_w_128x128(dev16(dec.w[e]))
+            d_wq[e].copy_(q_e)
+            d_ws[e].copy_(s_e)
+        d_y = torch.empty((m_d, N_d), dtype=torch.bfloat16, device=dev)
+        d_off = [int(v) for v in dec.row_off]
+        nbytes = (G_d * N_d * K_d + G_d * (N_d // 128) * (K_d // 128) * 4 + m_d * K_d + m_d * (K_d // 128) * 4
+                  + m_d * N_d * 2)
+
+        def fn():
+            fb.fp8bq_grouped_gemm_decode(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
+                                         d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d, 0, sp)
+    else:   # mfma_stream: the matrix-unit probe without promotion (reference for the busy counters)
+        from fp8_fine_grained_fp8bq_amd import probe
+        codes = torch.randint(0, 0x7F, (1 << 22,), dtype=torch.uint8, device=dev)
+        pscales = torch.full((64,), 1e-3, dtype=torch.float32, device=dev)
+        sink = torch.empty((256 * 512,), dtype=torch.float32, device=dev)
+        ticks = torch.zeros((512,), dtype=torch.int64, device=dev)
+        iters = 2000
+        flops = 2.0 * 16 * 16 * 128 * 32 * 8 * 256 * iters
+
+        def fn():
+            probe.fp8bq_probe_mfma_stream(0, iters, 256, codes.data_ptr(), pscales.data_ptr(), sink.data_ptr(),
+                                          ticks.data_ptr(), sp)
+
+    fn()
+    torch.cuda.synchronize()
+    # bring the clock to its sustained-load value first (untimed launches, about 300 ms)
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    first = max(time.perf_counter() - t0, 1e-5)
+    for _ in range(min(400, int(0.3 / first) + 1)):
+        if cold:
+            flush.sum()
+        fn()
+    torch.cuda.synchronize()
+    us = []
+    for _ in range(args.leg_reps):
+        if cold:
+            flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3)
+    med = float(np.median(us))
+    out = {"leg": leg, "reps": args.leg_reps, "us_median": round(med, 2), "us": [round(u, 2) for u in us]}
+    if flops:
+        out["TFLOPs"] = round(flops / (med * 1e-6) / 1e12, 1)
+        out["flops_per_launch"] = flops
+    if nbytes:
+        out["GBps"] = round(nbytes / med / 1e3, 1)
+        out["bytes_per_launch"] = nbytes
+    print(json.dumps(out), flush=True)
 
 
 # every file whose change alters the GEMM kernel's code (the counters taken for one
@@ -155,6 +323,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.leg:
+        run_leg(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
