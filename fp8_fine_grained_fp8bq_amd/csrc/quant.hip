@@ -103,7 +103,13 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 // transposed output, so each wave writes 128-byte runs of 16 output rows.
 // ---------------------------------------------------------------------------
 constexpr int kColBlockCols = 64;
-constexpr int kColLdsStride = kColBlockCols / 2 + 1;   // dwords per staged row (+1 pad)
+constexpr int kColLdsStride = kColBlockCols / 2;       // dwords per staged row
+// Column pair c of staged row r sits at dword c ^ col_swz(r) of the row. A
+// staging store puts 4 rows x 8 column quads in one half-wave, and the column
+// reads put 8 row groups (16 rows apart) x 4 column pairs in one: with this
+// XOR each touches 32 distinct banks (a padded stride cannot do both: 16 rows
+// apart is a multiple of 16 banks for any odd stride).
+__device__ __forceinline__ int col_swz(int r) { return ((r >> 2) & 0x1C) | (r & 3); }
 
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
@@ -119,8 +125,9 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const int row = i * 32 + (t >> 3);
     const int d = (t & 7) * 4;
     const uint4 w = *reinterpret_cast<const uint4*>(x + (r0 + row) * ldx + c0 + d * 2);
-    uint32_t* dst = tile + row * kColLdsStride + d;
-    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+    uint32_t* dst = tile + row * kColLdsStride;
+    const int f = col_swz(row);
+    dst[(d + 0) ^ f] = w.x; dst[(d + 1) ^ f] = w.y; dst[(d + 2) ^ f] = w.z; dst[(d + 3) ^ f] = w.w;
   }
   __syncthreads();
 
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   uint32_t mlo = 0, mhi = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    w[i] = tile[(seg * 16 + i) * kColLdsStride + p];
+    w[i] = tile[(seg * 16 + i) * kColLdsStride + (p ^ col_swz(seg * 16 + i))];
     mlo = umax(mlo, w[i] & 0x7FFFu);
     mhi = umax(mhi, (w[i] >> 16) & 0x7FFFu);
   }
