@@ -62,6 +62,8 @@ def parse():
                     help="only launch one kernel of the bench (after one untimed launch) --leg-reps times: "
                          "the command the counter summaries under profiles/ are taken with")
     ap.add_argument("--leg-reps", type=int, default=5)
+    ap.add_argument("--status-table", metavar="JSON", default=None,
+                    help="print the measured-status rows (markdown) of a file holding this script's JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -82,6 +84,84 @@ def calibrate_copy():
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def status_table(path):
+    """Markdown rows of the measured status, generated from a bench JSON line (the last
+    line of `path` that parses as one), so that no figure is copied by hand."""
+    d = None
+    for line in open(path).read().splitlines():
+        try:
+            v = json.loads(line)
+        except ValueError:
+            continue
+        if isinstance(v, dict) and "roofline" in v:
+            d = v
+    if d is None:
+        raise SystemExit(f"{path}: no bench JSON line")
+
+    def spread(st):
+        return f"median {st['median']:.1f}, p10 {st['p10']:.1f}, p90 {st['p90']:.1f}" if st else ""
+
+    def pct(x):
+        return f"{100 * x:.1f}%"
+
+    rows = []
+    r, b, o, v = d["roofline"], d["breakdown"], d.get("other_configs", {}), d.get("variants", {})
+    clk = (f"; {pct(r['frac_at_measured_clock'])} of the peak at the measured {r['clock_ghz']:.3f} GHz"
+           if r.get("clock_ghz") else "")
+    rows.append(("a6–a8 Fprop GEMM, large (16384×18432×7168)", r["kernel"],
+                 f"{r['avg_us']:.1f} µs ({spread(r.get('us_stats'))}), {r['achieved']:.0f} TFLOP/s = "
+                 f"{pct(r['frac'])} of 5.0 PF{clk}"))
+    rows.append(("step: quant X + quant W + GEMM", "three kernels",
+                 f"{d['ms_per_step']:.3f} ms, **{d['value']:.0f} TFLOP/s incl. quant = {pct(b['frac_of_fp8_peak_incl_quant'])}"
+                 f" of 5.0 PF**"))
+    for key, name, kern in (("quant_act", "a1–a3 activation 1×128 quantisation, X [16384, 7168]", "quant_act_rows_kernel"),
+                            ("quant_w", "a4 weight 128×128 quantisation, W [18432, 7168]", "quant_w2_kernel")):
+        rows.append((name, kern, f"{b[key + '_us']:.1f} µs cold ({spread(b.get(key + '_us_stats'))}), "
+                                 f"{b[key + '_GBps'] / 1000:.2f} TB/s = {pct(b[key + '_frac_hbm'])} of 8 TB/s, "
+                                 f"{pct(b[key + '_frac_ceiling'])} of the measured 2:1 streaming ceiling"))
+    if "quant_act_128x1" in o:
+        q = o["quant_act_128x1"]
+        rows.append(("a5 128×1 token-direction quantisation, X [4096, 7168]", "quant_act_cols_kernel",
+                     f"{q['us']:.1f} µs cold, {q['GBps'] / 1000:.2f} TB/s = {pct(q['frac_hbm'])} of 8 TB/s"))
+    for key, name, kern in (("dense_fprop", "a6–a8 Fprop GEMM, dense (4096×2048×7168)", "gemm_kernel<FPROP>, 256×128 tiles"),
+                            ("dgrad", "a6–a8 Dgrad GEMM (4096×7168×2048)", "gemm_kernel<DGRAD>, 256×224 tiles"),
+                            ("wgrad", "a6–a8 Wgrad GEMM (2048×7168×4096, fp32 out)", "gemm_kernel<WGRAD>, 256×224 tiles")):
+        if key in o:
+            g = o[key]
+            rows.append((name, kern, f"{g['us']:.1f} µs, {g['TFLOPs']:.0f} TFLOP/s = {pct(g['frac_fp8_peak'])} of 5.0 PF"))
+    if "moe_grouped" in o:
+        g = o["moe_grouped"]
+        rows.append(("a9 grouped MoE Fprop (8 experts, 54 400 padded rows)", "gemm_kernel<FPROP, grouped>",
+                     f"{g['us']:.1f} µs, {g['TFLOPs_routed_rows']:.0f} TFLOP/s on the routed rows = "
+                     f"{pct(g['frac_fp8_peak_routed'])} of 5.0 PF"))
+    if "requant_t_us" in b:
+        rows.append(("NEXT-1 cache re-quantisation 1×128 → 128×1, X [16384, 7168]", "requant_t_kernel",
+                     f"{b['requant_t_us']:.1f} µs cold, {b['requant_t_GBps'] / 1000:.2f} TB/s = "
+                     f"{pct(b['requant_t_frac_hbm'])} of 8 TB/s"))
+    if "pow2_scales" in v:
+        g = v["pow2_scales"]
+        rows.append(("NEXT-2 power-of-two scales (large fprop)", g["kernel"],
+                     f"GEMM {g['gemm_us']:.1f} µs, {g['gemm_TFLOPs']:.0f} TFLOP/s = {pct(g['gemm_TFLOPs'] / PEAK_FP8_TFLOPS)}"
+                     f" of 5.0 PF; step {g['ms_per_step']:.3f} ms, {g['value']:.0f} TFLOP/s incl. quant"))
+    if "producer_fusion" in v:
+        g = v["producer_fusion"]
+        rows.append(("NEXT-3 producer fusion (large fprop)", g["kernel"],
+                     f"fused {g['fused_us']:.1f} µs against {g['separate_us']:.1f} µs for GEMM + quantiser of its output;"
+                     f" {g['hbm_bytes_saved'] / 1e9:.2f} GB less HBM traffic per launch"))
+    if "decode_grouped" in v:
+        g = v["decode_grouped"]
+        rows.append(("NEXT-4 decode grouped Fprop (853 rows, 8 × [2048, 7168])", g["kernel"],
+                     f"{g['us']:.1f} µs cold ({spread(g.get('us_stats'))}), {g['GBps'] / 1000:.2f} TB/s = "
+                     f"{pct(g['roofline']['frac'])} of 8 TB/s"))
+    c = d.get("cpu_baseline")
+    if c:
+        rows.append(("CPU oracle (numpy)", "oracle/", f"{c['value'] * 1000:.1f} GFLOP/s on {c['cores']} host threads ({c['sample']})"))
+    print("| row | kernel | measured |")
+    print("|---|---|---|")
+    for row in rows:
+        print("| " + " | ".join(row) + " |")
 
 
 # kernels that --leg launches alone (each on the workload the bench times it on)
@@ -321,6 +401,9 @@ def cpu_threads() -> int:
 
 def main():
     args = parse()
+    if args.status_table:
+        status_table(args.status_table)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return
