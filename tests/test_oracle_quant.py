@@ -35,13 +35,27 @@ def test_absmax_element_maps_to_448():
         assert np.all((qq[hit] >> 7) == (xf[hit] < 0))
 
 
+def _f32_of_fraction(fr):
+    """Nearest binary32 of an exact rational that is never a binary32 midpoint.
+    Rounding to binary64 first cannot land on a binary32 midpoint here: the
+    quotients below have an odd factor (7, or the odd part of a 24-bit scale)
+    in the denominator, so their binary expansions are not dyadic and do not
+    hold 28 zero bits after the 25th significant bit."""
+    return np.float32(float(fr))
+
+
 def test_scale_definition_and_layout():
+    # s is the binary32 rounding of the exact rational absmax / 448, computed
+    # here with fractions rather than with the oracle's float32 division
+    from fractions import Fraction
     x = _x()
     q, s = quant.quant_act_1x128(x)
     xf = quant.bf16_bits_to_f32(x).reshape(x.shape[0], -1, 128)
-    want = (np.abs(xf).max(-1) / np.float32(448.0)).astype(np.float32)
-    np.testing.assert_array_equal(s, want)
     assert s.shape == (64, 4) and s.dtype == np.float32
+    for r in range(0, 64, 7):
+        for t in range(4):
+            amax = max(abs(Fraction(float(v))) for v in xf[r, t])
+            assert s[r, t] == _f32_of_fraction(amax / 448), (r, t)
 
 
 def test_dequant_error_bound():
@@ -100,13 +114,15 @@ def test_weight_block_transpose_invariance():
 
 
 def test_weight_block_scale_is_block_absmax():
+    from fractions import Fraction
     w = act(14, 256, 256, std=0.02)
     q, s = quant.quant_w_128x128(w)
     wf = quant.bf16_bits_to_f32(w)
     for i in range(2):
         for j in range(2):
             blk = wf[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
-            assert s[i, j] == np.float32(np.abs(blk).max()) / np.float32(448)
+            amax = max(abs(Fraction(float(v))) for v in blk.ravel()[np.argsort(-np.abs(blk.ravel()))[:4]])
+            assert s[i, j] == _f32_of_fraction(amax / 448)
             # a 128x128 block is not 128 independent 1x128 tiles: rows share one scale
             qa, sa = quant.quant_act_1x128(f32_to_bf16_bits(blk))
             assert not np.all(sa == s[i, j])
@@ -143,10 +159,16 @@ def test_128x1_is_quantisation_along_rows():
     qT, sT = quant.quant_act_128x1(x)
     assert qT.shape == (128, 256) and sT.shape == (128, 2)
     xf = quant.bf16_bits_to_f32(x)
+    # scales from exact rationals, codes from the brute-force nearest-value
+    # search on the binary32 quotient (reading 3), neither through the
+    # oracle's own arithmetic
+    from fractions import Fraction
     for j in (0, 77):
         for c in range(2):
             col = xf[c * 128:(c + 1) * 128, j]
-            assert sT[j, c] == np.float32(np.abs(col).max()) / np.float32(448)
-            s = sT[j, c]
-            np.testing.assert_array_equal(qT[j, c * 128:(c + 1) * 128],
-                                          e4m3.encode((col / s).astype(np.float32)))
+            amax = max(abs(Fraction(float(v))) for v in col)
+            assert sT[j, c] == _f32_of_fraction(amax / 448)
+            s = Fraction(float(sT[j, c]))
+            want = [e4m3.encode_bruteforce(float(_f32_of_fraction(Fraction(float(v)) / s))) if v != 0
+                    else (0x80 if np.signbit(v) else 0x00) for v in col]
+            np.testing.assert_array_equal(qT[j, c * 128:(c + 1) * 128], np.array(want, np.uint8))
