@@ -140,6 +140,12 @@ def status_table(path):
         rows.append(("NEXT-1 cache re-quantisation 1×128 → 128×1, X [16384, 7168]", "requant_t_kernel",
                      f"{b['requant_t_us']:.1f} µs cold, {b['requant_t_GBps'] / 1000:.2f} TB/s = "
                      f"{pct(b['requant_t_frac_hbm'])} of 8 TB/s"))
+    if "e5m6_cache" in v:
+        g = v["e5m6_cache"]
+        rows.append(("A11 E5M6 activation cache 1×128, X [16384, 7168]", g["kernel"],
+                     f"cache {g['cache_us']:.1f} µs cold, {g['cache_GBps'] / 1000:.2f} TB/s = {pct(g['cache_frac_hbm'])}"
+                     f" of 8 TB/s; read back {g['read_back_us']:.1f} µs, {g['read_back_GBps'] / 1000:.2f} TB/s = "
+                     f"{pct(g['read_back_frac_hbm'])}"))
     if "pow2_scales" in v:
         g = v["pow2_scales"]
         rows.append(("NEXT-2 power-of-two scales (large fprop)", g["kernel"],
@@ -165,7 +171,8 @@ def status_table(path):
 
 
 # kernels that --leg launches alone (each on the workload the bench times it on)
-LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "mfma_stream")
+LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "mfma_stream",
+        "cache_e5m6", "uncache_e5m6")
 
 
 def run_leg(args):
@@ -184,14 +191,34 @@ def run_leg(args):
     torch.cuda.set_device(0)
     sp = torch.cuda.current_stream(dev).cuda_stream
     leg = args.leg
-    cold = leg in ("quant_x", "quant_w", "qcol", "decode")
+    cold = leg in ("quant_x", "quant_w", "qcol", "decode", "cache_e5m6", "uncache_e5m6")
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
     flops = nbytes = None
 
     def dev16(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
 
-    if leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
+    if leg in ("cache_e5m6", "uncache_e5m6"):
+        cfg = workloads.large_fprop()
+        _, M, _, K = WORKLOADS["large"]
+        x = dev16(cfg.x)
+        ldq_e = (K * 3 // 2 + 15) // 16 * 16
+        xe = torch.empty((M, ldq_e), dtype=torch.uint8, device=dev)
+        xes = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        yb = torch.empty((M, K), dtype=torch.int16, device=dev)
+        nbytes = M * K * 2 + M * (K * 3 // 2) + M * (K // 128) * 4
+
+        def cache():
+            fb.fp8bq_cache_e5m6_1x128(x.data_ptr(), M, K, K, xe.data_ptr(), ldq_e, xes.data_ptr(), M, sp)
+
+        def uncache():
+            fb.fp8bq_uncache_e5m6_1x128(xe.data_ptr(), M, K, ldq_e, xes.data_ptr(), M, yb.data_ptr(), K, sp)
+        if leg == "cache_e5m6":
+            fn = cache
+        else:
+            cache()
+            fn = uncache
+    elif leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
         cfg = workloads.large_fprop()
         _, M, N, K = WORKLOADS["large"]
         x, w = dev16(cfg.x), dev16(cfg.w)
@@ -569,6 +596,29 @@ def main():
     t_rq = st_t_rq["mean"]
     bytes_rq = 2 * M * K + 2 * (M * (K // 128) * 4)
     log(f"[bench] requant 1x128 -> 128x1: {t_rq:.1f} us ({bytes_rq / t_rq / 1e3:.0f} GB/s)")
+    del xqt, xst
+
+    # E5M6 activation cache of X (1x128 tiles, power-of-two scales, 12-bit codes
+    # packed two per 3 bytes) and its inverse, both cold
+    nb_e = K * 3 // 2
+    ldq_e = (nb_e + 15) // 16 * 16
+    xe = torch.empty((M, ldq_e), dtype=torch.uint8, device=dev)
+    xes = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+
+    def cache_e5m6():
+        fb.fp8bq_cache_e5m6_1x128(x.data_ptr(), M, K, K, xe.data_ptr(), ldq_e, xes.data_ptr(), M, sp)
+
+    def uncache_e5m6():
+        fb.fp8bq_uncache_e5m6_1x128(xe.data_ptr(), M, K, ldq_e, xes.data_ptr(), M, y.data_ptr(), K, sp)
+
+    cache_e5m6()
+    st_t_ce = time_kernel(cache_e5m6, args.kernel_reps, True)
+    uncache_e5m6()
+    st_t_ue = time_kernel(uncache_e5m6, args.kernel_reps, True)
+    bytes_e5m6 = M * K * 2 + M * nb_e + M * (K // 128) * 4
+    log(f"[bench] E5M6 cache {st_t_ce['mean']:.1f} us, read back {st_t_ue['mean']:.1f} us "
+        f"({bytes_e5m6 / st_t_ce['mean'] / 1e3:.0f} / {bytes_e5m6 / st_t_ue['mean'] / 1e3:.0f} GB/s)")
+    del xe, xes
 
     # producer fusion: the GEMM quantises its own output (1x128 tiles) for the
     # next GEMM, against the GEMM followed by the quantiser of its bf16 output
@@ -941,6 +991,19 @@ def main():
                 "fused_TFLOPs": round(flops / (t_fq * 1e-6) / 1e12, 1),
                 "hbm_bytes_saved": 4 * M * N,
                 "kernel": "gemm_kernel<FPROP, QMODE=1>",
+            },
+            "e5m6_cache": {
+                "what": f"E5M6 activation cache of X [{M}, {K}]: 1x128 tiles, power-of-two scales, 12-bit codes "
+                        "packed two per 3 bytes (read 2 B, write 1.5 B per element), and reading it back to bf16; "
+                        "cold",
+                "cache_us": round(st_t_ce["mean"], 2), "cache_us_stats": rnd(st_t_ce),
+                "cache_GBps": round(bytes_e5m6 / st_t_ce["mean"] / 1e3, 1),
+                "cache_frac_hbm": round(bytes_e5m6 / st_t_ce["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+                "read_back_us": round(st_t_ue["mean"], 2), "read_back_us_stats": rnd(st_t_ue),
+                "read_back_GBps": round(bytes_e5m6 / st_t_ue["mean"] / 1e3, 1),
+                "read_back_frac_hbm": round(bytes_e5m6 / st_t_ue["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes": bytes_e5m6,
+                "kernel": "cache_e5m6_kernel / uncache_e5m6_kernel",
             },
             "decode_grouped": {
                 "what": f"{dec.name}: rows per expert {[int(c) for c in dec.real_rows]} (unpadded), "

@@ -10,10 +10,12 @@ Two layers with the C names:
 
 * `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
   `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`,
-  `fp8bq_grouped_gemm_decode`: pointer-level, exactly the C signatures (ints
+  `fp8bq_grouped_gemm_decode`, `fp8bq_cache_e5m6_1x128`,
+  `fp8bq_uncache_e5m6_1x128`: pointer-level, exactly the C signatures (ints
   for pointers and the stream); a non-zero status raises `Fp8bqError`.
 * `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
-  `gemm_quant`, `grouped_gemm`, `grouped_gemm_decode`: take torch tensors on
+  `gemm_quant`, `grouped_gemm`, `grouped_gemm_decode`, `cache_e5m6_1x128`,
+  `uncache_e5m6_1x128`: take torch tensors on
   the GPU, allocate the outputs with torch (memory and streams are the only
   things torch provides) and call the same entry points on the current stream.
 """
@@ -33,8 +35,8 @@ ACT_ROWWISE, ACT_COLWISE = 0, 1
 SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_last_error",
-           "fp8bq_version")
+           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_cache_e5m6_1x128",
+           "fp8bq_uncache_e5m6_1x128", "fp8bq_last_error", "fp8bq_version")
 
 
 class Fp8bqError(RuntimeError):
@@ -58,13 +60,15 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_quant_act_1x128.argtypes = [vp, i64, i64, i64, i32, vp, i64, fp, i64, vp]
         L.fp8bq_quant_w_128x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         L.fp8bq_requant_t_128x1.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, fp, i64, i32, vp]
+        L.fp8bq_cache_e5m6_1x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp]
+        L.fp8bq_uncache_e5m6_1x128.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, vp]
         L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
         L.fp8bq_gemm_quant.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64,
                                        vp, i64, fp, i64, i32, vp]
         L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
                                          vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-                  "fp8bq_grouped_gemm"):
+                  "fp8bq_grouped_gemm", "fp8bq_cache_e5m6_1x128", "fp8bq_uncache_e5m6_1x128"):
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
         L.fp8bq_grouped_gemm_decode.argtypes = L.fp8bq_grouped_gemm.argtypes
@@ -182,6 +186,42 @@ def quant_w_128x128(w, transposed_copy: bool = False, pow2: bool = False):
     fp8bq_quant_w_128x128(w.data_ptr(), n, k, w.stride(0), q.data_ptr(), k, s.data_ptr(), k // 128,
                           qt.data_ptr() if qt is not None else None, n, SCALE_POW2 if pow2 else 0, _stream(w))
     return q, s, qt
+
+
+def fp8bq_cache_e5m6_1x128(x, rows, cols, ldx, q, ldq, s, lds, stream=0):
+    return _check("fp8bq_cache_e5m6_1x128", lib().fp8bq_cache_e5m6_1x128(x, rows, cols, ldx, q, ldq, s, lds, stream))
+
+
+def fp8bq_uncache_e5m6_1x128(q, rows, cols, ldq, s, lds, y, ldy, stream=0):
+    return _check("fp8bq_uncache_e5m6_1x128",
+                  lib().fp8bq_uncache_e5m6_1x128(q, rows, cols, ldq, s, lds, y, ldy, stream))
+
+
+def cache_e5m6_1x128(x):
+    """bf16 [rows, cols] (int16/bfloat16 storage) -> (q uint8 [rows, 1.5 cols]: packed 12-bit E5M6
+    codes, s float32 [cols/128, rows]: chunk-major power-of-two 1x128 tile scales)."""
+    import torch
+    if x.dim() != 2 or x.element_size() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D row-major 16-bit tensor of bf16 patterns")
+    rows, cols = x.shape
+    ldq = (cols * 3 // 2 + 15) // 16 * 16
+    q = torch.empty((rows, ldq), dtype=torch.uint8, device=x.device)
+    s = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+    fp8bq_cache_e5m6_1x128(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), ldq, s.data_ptr(), rows, _stream(x))
+    return q[:, : cols * 3 // 2], s
+
+
+def uncache_e5m6_1x128(q, s, cols):
+    """Packed E5M6 codes q (rows of >= 1.5 cols bytes, row stride q.stride(0)) and their scales s
+    [cols/128, >=rows] -> bf16 [rows, cols] (torch.bfloat16)."""
+    import torch
+    if q.dtype != torch.uint8 or q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError("q must be a 2-D row-major uint8 tensor")
+    rows = q.shape[0]
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.device)
+    fp8bq_uncache_e5m6_1x128(q.data_ptr(), rows, cols, q.stride(0), s.data_ptr(), s.stride(0), y.data_ptr(), cols,
+                             _stream(q))
+    return y
 
 
 def requant_t_128x1(q, s):

@@ -107,6 +107,37 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
                                                static_cast<uint8_t*>(q), ldq, s, lds, pow2, str), "quant_act");
 }
 
+static int check_e5m6(const char* who, const void* a, const void* b, const float* s, int64_t rows, int64_t cols,
+                      int64_t ld16, int64_t ldq, int64_t lds) {
+  if (!a || !b || !s) return fail(FP8BQ_E_INVAL, "%s: null pointer", who);
+  if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "%s: rows and cols must be positive", who);
+  if (cols % 128) return fail(FP8BQ_E_SHAPE, "%s: cols (%lld) must be a multiple of 128", who, (long long)cols);
+  if (ld16 < cols) return fail(FP8BQ_E_INVAL, "%s: bf16 leading dimension < cols", who);
+  if (ldq / 3 < cols / 2) return fail(FP8BQ_E_INVAL, "%s: ldq (bytes) < 1.5 * cols", who);   // ldq < 3 (cols / 2)
+  if (lds < rows) return fail(FP8BQ_E_INVAL, "%s: lds < rows", who);
+  if (rows >= kMaxTiles || product_at_least(ceil_div(rows, 32), cols / 128, kMaxTiles))
+    return fail(FP8BQ_E_SHAPE, "%s: too large", who);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(s, 4))
+    return fail(FP8BQ_E_ALIGN, "%s: bf16 and code buffers must be 16-byte aligned, s 4-byte aligned", who);
+  if (ld16 % 8 || ldq % 16) return fail(FP8BQ_E_ALIGN, "%s: bf16 ld must be a multiple of 8 and ldq of 16", who);
+  return check_device();
+}
+
+int fp8bq_cache_e5m6_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, int64_t ldq, float* s,
+                           int64_t lds, void* stream) {
+  if (int st = check_e5m6("cache_e5m6", x, q, s, rows, cols, ldx, ldq, lds)) return st;
+  return launched(fp8bq::launch_cache_e5m6(static_cast<const uint16_t*>(x), rows, cols, ldx, static_cast<uint8_t*>(q),
+                                           ldq, s, lds, reinterpret_cast<hipStream_t>(stream)), "cache_e5m6");
+}
+
+int fp8bq_uncache_e5m6_1x128(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
+                             void* y, int64_t ldy, void* stream) {
+  if (int st = check_e5m6("uncache_e5m6", y, q, s, rows, cols, ldy, ldq, lds)) return st;
+  return launched(fp8bq::launch_uncache_e5m6(static_cast<const uint8_t*>(q), rows, cols, ldq, s, lds,
+                                             static_cast<uint16_t*>(y), ldy, reinterpret_cast<hipStream_t>(stream)),
+                  "uncache_e5m6");
+}
+
 int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
                           void* qt, int64_t ldqt, float* st, int64_t ldst, int flags, void* stream) {
   if (!q || !s || !qt || !st) return fail(FP8BQ_E_INVAL, "requant_t: null pointer");

@@ -20,6 +20,13 @@ hipError_t launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, 
 hipError_t launch_requant_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
                             int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream);
 
+// E5M6 activation cache: bf16 [rows, cols] -> packed 12-bit codes (1.5 B per
+// element, ldq in bytes) + chunk-major power-of-two scales, and back to bf16.
+hipError_t launch_cache_e5m6(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, int64_t lds, hipStream_t st);
+hipError_t launch_uncache_e5m6(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                               int64_t lds, uint16_t* y, int64_t ldy, hipStream_t st);
+
 enum GemmKind { KIND_FPROP = 0, KIND_DGRAD = 1, KIND_WGRAD = 2 };
 
 hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,

@@ -14,6 +14,9 @@
 #include "internal.h"
 #include "fp8_codec.h"
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 namespace fp8bq {
 namespace {
 
@@ -386,6 +389,136 @@ __global__ __launch_bounds__(256) void quant_w2_kernel(
     *reinterpret_cast<uint2*>(q + (n0 + wv * 32 + 2 * i + (lane >> 5)) * ldq + col) = encode8<POW2>(v[i], ts);
 }
 
+
+// ---------------------------------------------------------------------------
+// E5M6 activation cache (report section 3.3.3, low-precision activations,
+// item 1: the inputs of the Linear after attention are cached in a custom
+// 12-bit E5M6 format, in 1x128 tiles with power-of-two scaling factors).
+// E5M6: 1 sign, 5 exponent (bias 15), 6 mantissa bits, the binary16 layout
+// without its four lowest mantissa bits; subnormals m * 2^-20; largest finite
+// value 65024. Tile scale s = 2^k, k the smallest integer with absmax <=
+// 65024 * 2^k, clamped to [-127, 127]; codes E5M6(x * 2^-k), rounded to
+// nearest even once (the product is exact). Codes are packed two per 3 bytes,
+// little-endian in the 24-bit group, so a tile is 192 contiguous bytes.
+// ---------------------------------------------------------------------------
+
+// k of the tile from its bf16 absmax bits (no sign). absmax = f * 2^(e - 127)
+// with f = 1 + m / 128; 65024 = (127/64) * 2^15, so k = e - 142, plus one when
+// f > 127/64 (m = 127). A zero or subnormal absmax is at most 65024 * 2^-127.
+__device__ __forceinline__ int e5m6_tile_exponent(uint32_t amax16) {
+  const int e = (int)(amax16 >> 7);
+  if (e == 0) return -127;
+  const int k = e - 142 + ((amax16 & 0x7Fu) == 0x7Fu ? 1 : 0);
+  return k < -127 ? -127 : k;
+}
+
+// 2^j as a float for j in [-127, 127] (2^-127 is subnormal).
+__device__ __forceinline__ float exp2_int(int j) {
+  return j >= -126 ? __uint_as_float((uint32_t)(j + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// E5M6 code of v, |v| <= 65024: round to nearest even, sign kept. Normal
+// range (|v| >= 2^-14): the fp32 mantissa rounded to 6 bits (a carry moves
+// into the exponent), exponent rebiased 127 -> 15; below it, the nearest
+// multiple of 2^-20 (64 of them is the smallest normal, whose code is 64).
+__device__ __forceinline__ uint32_t e5m6_code(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 20) & 0x800u;
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  const uint32_t cn = ((mag + 0xFFFFu + ((mag >> 17) & 1u)) >> 17) - (112u << 6);
+  const uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 1048576.0f);   // exact product
+  return (mag >= 0x38800000u ? cn : cs) | sign;   // both formed: no divergent branch
+}
+
+// Value of an E5M6 code (exponent field 31 is never written).
+__device__ __forceinline__ float e5m6_value(uint32_t c) {
+  const uint32_t e = (c >> 6) & 31u, m = c & 63u;
+  const float f = e ? __uint_as_float(((e + 112u) << 23) | (m << 17)) : (float)m * 0x1p-20f;
+  return __uint_as_float(__float_as_uint(f) | ((c & 0x800u) << 20));
+}
+
+// A tile per 16-lane DPP row, 8 elements per lane: a lane loads 16 B of bf16
+// and stores its 12 code bytes next to its neighbours', so one store
+// instruction writes each tile's 192 bytes contiguously (with 24-byte lanes,
+// three 8-byte stores each covering every third piece of the tile ran the
+// cache at 83 us on X [16384, 7168]). A 256-thread block covers 16 rows of one
+// 128-column chunk (4 per wave).
+constexpr int kE5RowsPerBlock = kRowThreads / 16;
+
+__device__ __forceinline__ uint32_t mag_max8(const uint4 a) {
+  auto m = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
+  const u16x2 r = __builtin_elementwise_max(__builtin_elementwise_max(m(a.x), m(a.y)),
+                                            __builtin_elementwise_max(m(a.z), m(a.w)));
+  return umax(r.x, r.y);
+}
+
+// A thread takes NT neighbouring tiles of its row (NT = 2 when the row has an
+// even number of tiles: two loads in flight per lane, as in the FP8 kernel).
+template <int NT>
+__global__ __launch_bounds__(kRowThreads) void cache_e5m6_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int rows, int tpr, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s, int64_t lds) {
+  const int l16 = threadIdx.x & 15;
+  const int groups = tpr / NT;
+  const int group = (int)(blockIdx.x / (unsigned)groups);
+  const int col0 = (int)(blockIdx.x - (unsigned)group * (unsigned)groups) * NT;
+  const int r = group * kE5RowsPerBlock + (threadIdx.x >> 4);
+  const int row = r < rows ? r : rows - 1;
+  uint4 v[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    v[t] = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (col0 + t) * 128 + l16 * 8);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int k = e5m6_tile_exponent(row16_max(mag_max8(v[t])));
+    const float inv = exp2_int(-k);
+    const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+    uint32_t pr[4];   // element pairs (2i, 2i + 1) as 24-bit groups
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = e5m6_code(bf_lo(w[i]) * inv) | (e5m6_code(bf_hi(w[i]) * inv) << 12);
+    if (r < rows) {
+      *reinterpret_cast<uint3*>(q + (int64_t)row * ldq + (col0 + t) * 192 + l16 * 12) =
+          make_uint3(pr[0] | (pr[1] << 24), (pr[1] >> 8) | (pr[2] << 16), (pr[2] >> 16) | (pr[3] << 8));
+      if (l16 == 0) s[(int64_t)(col0 + t) * lds + row] = exp2_int(k);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(kRowThreads) void uncache_e5m6_kernel(
+    const uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ s, int64_t lds, int rows, int tpr,
+    uint16_t* __restrict__ y, int64_t ldy) {
+  const int l16 = threadIdx.x & 15;
+  const int groups = tpr / NT;
+  const int group = (int)(blockIdx.x / (unsigned)groups);
+  const int col0 = (int)(blockIdx.x - (unsigned)group * (unsigned)groups) * NT;
+  const int r = group * kE5RowsPerBlock + (threadIdx.x >> 4);
+  if (r >= rows) return;
+  uint3 in[NT];
+  float sc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    in[t] = *reinterpret_cast<const uint3*>(q + (int64_t)r * ldq + (col0 + t) * 192 + l16 * 12);
+    sc[t] = s[(int64_t)(col0 + t) * lds + r];
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint3 i = in[t];
+    const uint32_t pr[4] = {i.x & 0xFFFFFFu, (i.x >> 24) | ((i.y & 0xFFFFu) << 8),
+                            (i.y >> 16) | ((i.z & 0xFFu) << 16), i.z >> 8};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // exact products (7 significant bits times a power of two within range),
+      // then one rounding to bf16
+      const bf16x2 h = __builtin_convertvector(
+          (f32x2){e5m6_value(pr[j] & 0xFFFu) * sc[t], e5m6_value(pr[j] >> 12) * sc[t]}, bf16x2);
+      __builtin_memcpy(&o[j], &h, 4);
+    }
+    *reinterpret_cast<uint4*>(y + (int64_t)r * ldy + (col0 + t) * 128 + l16 * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -433,6 +566,34 @@ hipError_t launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, 
     hipLaunchKernelGGL(quant_w_kernel<true>, grid, dim3(256), 0, st, w, ldw, q, ldq, s, lds, qt, ldqt);
   else
     hipLaunchKernelGGL(quant_w_kernel<false>, grid, dim3(256), 0, st, w, ldw, q, ldq, s, lds, qt, ldqt);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_e5m6(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                             float* s, int64_t lds, hipStream_t st) {
+  const int tpr = (int)(cols / 128);
+  const int nt = tpr % 4 == 0 ? 4 : tpr % 2 == 0 ? 2 : 1;
+  const dim3 grid((unsigned)((rows + kE5RowsPerBlock - 1) / kE5RowsPerBlock * (tpr / nt)));
+  if (nt == 4)
+    hipLaunchKernelGGL(cache_e5m6_kernel<4>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, tpr, q, ldq, s, lds);
+  else if (nt == 2)
+    hipLaunchKernelGGL(cache_e5m6_kernel<2>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, tpr, q, ldq, s, lds);
+  else
+    hipLaunchKernelGGL(cache_e5m6_kernel<1>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, tpr, q, ldq, s, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_uncache_e5m6(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                               int64_t lds, uint16_t* y, int64_t ldy, hipStream_t st) {
+  const int tpr = (int)(cols / 128);
+  const int nt = tpr % 4 == 0 ? 4 : tpr % 2 == 0 ? 2 : 1;
+  const dim3 grid((unsigned)((rows + kE5RowsPerBlock - 1) / kE5RowsPerBlock * (tpr / nt)));
+  if (nt == 4)
+    hipLaunchKernelGGL(uncache_e5m6_kernel<4>, grid, dim3(kRowThreads), 0, st, q, ldq, s, lds, (int)rows, tpr, y, ldy);
+  else if (nt == 2)
+    hipLaunchKernelGGL(uncache_e5m6_kernel<2>, grid, dim3(kRowThreads), 0, st, q, ldq, s, lds, (int)rows, tpr, y, ldy);
+  else
+    hipLaunchKernelGGL(uncache_e5m6_kernel<1>, grid, dim3(kRowThreads), 0, st, q, ldq, s, lds, (int)rows, tpr, y, ldy);
   return hipGetLastError();
 }
 

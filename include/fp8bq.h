@@ -104,6 +104,43 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
                           void* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
 /*
+ * E5M6 activation cache, 1x128 tiles (report section 3.3.3 "low-precision
+ * storage and communication", low-precision activations, item 1: the inputs of
+ * the Linear after the attention operator are cached in a custom 12-bit E5M6
+ * format, with power-of-two scaling factors so that turning the 1x128 tiles
+ * into 128x1 tiles in the backward pass adds no error).
+ *
+ * Format: 1 sign, 5 exponent (bias 15), 6 mantissa bits, the layout of IEEE
+ * binary16 without its four lowest mantissa bits; exponent field 0 holds
+ * subnormals m * 2^-20; largest finite value 65024; field 31 is never written.
+ * Tile scale s = 2^k, k the smallest integer with the tile's absmax <= 65024 *
+ * 2^k, within [-127, 127] (2^-127 for an all-zero tile); codes
+ * E5M6(x * 2^-k), the product exact, rounded to nearest even once, sign kept.
+ *
+ * x     bf16 [rows, cols], ldx >= cols (elements, multiple of 8).
+ * q     packed codes: row r at q + r * ldq (bytes), 1.5 * cols bytes per row;
+ *       elements 2i and 2i+1 of a row share bytes 3i .. 3i+2 (element 2i in
+ *       bits 0..11 of the little-endian 24-bit group). ldq >= 1.5 * cols, a
+ *       multiple of 16.
+ * s     float, tile (r, c) at s[c * lds + r], lds >= rows.
+ * cols must be a multiple of 128. The caller owns all buffers.
+ * Errors: E_INVAL (null, sizes <= 0, ld too small), E_SHAPE, E_ALIGN (x and q
+ *         16-byte aligned, s 4-byte aligned), E_DEVICE, E_HIP.
+ */
+int fp8bq_cache_e5m6_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                           void* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/*
+ * The inverse of fp8bq_cache_e5m6_1x128: y = bf16 round-to-nearest-even of
+ * E5M6(code) * s (the product is exact; it is the cached value itself whenever
+ * that lies in bf16's normal range). q, ldq, s, lds as written by the cache
+ * call; y bf16 [rows, cols], ldy >= cols (elements, multiple of 8), 16-byte
+ * aligned. Errors as fp8bq_cache_e5m6_1x128.
+ */
+int fp8bq_uncache_e5m6_1x128(const void* q, int64_t rows, int64_t cols, int64_t ldq,
+                             const float* s, int64_t lds, void* y, int64_t ldy, void* stream);
+
+/*
  * Transposing re-quantisation of an FP8 activation cache, 1x128 -> 128x1
  * (report section 3.5.2 "support for transposed GEMM": the forward pass keeps
  * activations as 1x128 FP8 tiles, the backward pass reads them, dequantises,

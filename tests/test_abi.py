@@ -110,6 +110,29 @@ def test_requant_validation(L):
     assert "too large" in L.fp8bq_last_error().decode()
 
 
+@pytest.mark.parametrize("f", ["fp8bq_cache_e5m6_1x128", "fp8bq_uncache_e5m6_1x128"])
+def test_e5m6_validation(L, f):
+    # rows, cols = 100, 384: bf16 [100, 384] ld 384; packed codes 576 bytes per row, ldq 576; s lds 100
+    cache = f == "fp8bq_cache_e5m6_1x128"
+    ok = ([A16, 100, 384, 384, B16, 576, S4, 100, None] if cache
+          else [B16, 100, 384, 576, S4, 100, A16, 384, None])
+    ld16, ldq, lds, p16, pq = (3, 5, 7, 0, 4) if cache else (7, 3, 5, 6, 0)
+    def bad(i, v):
+        a = list(ok); a[i] = v
+        return _st(L, f, *a)
+    assert bad(p16, None) == fb.E_INVAL
+    assert bad(1, 0) == fb.E_INVAL
+    assert bad(2, 300) == fb.E_SHAPE                                            # cols % 128
+    assert bad(ld16, 256) == fb.E_INVAL                                         # bf16 ld < cols
+    assert bad(ldq, 560) == fb.E_INVAL                                          # ldq < 1.5 cols
+    assert bad(lds, 99) == fb.E_INVAL                                           # lds < rows
+    assert bad(p16, A16 + 8) == fb.E_ALIGN
+    assert bad(pq, B16 + 4) == fb.E_ALIGN
+    assert bad(ldq, 584) == fb.E_ALIGN                                          # ldq % 16
+    assert bad(ld16, 388) == fb.E_ALIGN                                         # bf16 ld % 8
+    assert bad(6 if cache else 4, S4 + 2) == fb.E_ALIGN
+
+
 def _gemm_ok(op=0):
     # m, n, k = 300, 384, 1024
     ldsb = {0: 8, 1: 3, 2: 384}[op]
