@@ -115,7 +115,8 @@ static int check_e5m6(const char* who, const void* a, const void* b, const float
   if (ld16 < cols) return fail(FP8BQ_E_INVAL, "%s: bf16 leading dimension < cols", who);
   if (ldq / 3 < cols / 2) return fail(FP8BQ_E_INVAL, "%s: ldq (bytes) < 1.5 * cols", who);   // ldq < 3 (cols / 2)
   if (lds < rows) return fail(FP8BQ_E_INVAL, "%s: lds < rows", who);
-  if (rows >= kMaxTiles || product_at_least(ceil_div(rows, 32), cols / 128, kMaxTiles))
+  // the kernels run 16 rows of one 128-column chunk per workgroup: the grid holds ceil(rows / 16) * (cols / 128)
+  if (rows >= kMaxTiles || product_at_least(ceil_div(rows, 16), cols / 128, kMaxTiles))
     return fail(FP8BQ_E_SHAPE, "%s: too large", who);
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(s, 4))
     return fail(FP8BQ_E_ALIGN, "%s: bf16 and code buffers must be 16-byte aligned, s 4-byte aligned", who);

@@ -131,6 +131,11 @@ def test_e5m6_validation(L, f):
     assert bad(ldq, 584) == fb.E_ALIGN                                          # ldq % 16
     assert bad(ld16, 388) == fb.E_ALIGN                                         # bf16 ld % 8
     assert bad(6 if cache else 4, S4 + 2) == fb.E_ALIGN
+    # 2^20 rows x 32768 tiles per row: 2^30 workgroups of 32 rows but 2^31 of the kernels' 16 rows
+    rows, cols = 1 << 20, 128 * 32768
+    big = ([A16, rows, cols, cols, B16, cols * 3 // 2, S4, rows, None] if cache
+           else [B16, rows, cols, cols * 3 // 2, S4, rows, A16, cols, None])
+    assert _st(L, f, *big) == fb.E_SHAPE and "too large" in L.fp8bq_last_error().decode()
 
 
 def _gemm_ok(op=0):
