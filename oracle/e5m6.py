@@ -31,7 +31,10 @@ Pinned by tests/test_oracle_e5m6.py: the value set against numpy's binary16
 (every code's value is the binary16 value of the same bits shifted left by 4),
 closed forms (count of values, extremes), the brute-force nearest-value encoder
 on every bf16 pattern at several scales and on every rounding midpoint, a
-hand-packed example, and the round-trip error bound.
+hand-packed example, and the round-trip error bound; the backward conversion
+to 128x1 FP8 tiles against the separately pinned 128x1 power-of-two FP8
+quantiser applied to the cached values (exact in bf16 there) and against a
+hand-worked column.
 """
 
 from __future__ import annotations
@@ -205,3 +208,28 @@ def uncache_1x128(packed: np.ndarray, s: np.ndarray, cols: int) -> np.ndarray:
     rows = codes.shape[0]
     v = decode(codes).reshape(rows, cols // 128, 128)
     return (v * s.T.astype(np.float64)[..., None]).reshape(rows, cols)
+
+
+def requant_128x1(packed: np.ndarray, s: np.ndarray, cols: int) -> tuple[np.ndarray, np.ndarray]:
+    """The backward conversion of the cache (report section 3.3.3: the 1x128
+    tiles become 128x1 tiles, and the power-of-two scales keep the conversion
+    from adding an error of its own): x_hat = E5M6(code) * s exactly, 128x1
+    groups (128 consecutive rows of one column), the group's scale 2^k with k
+    the smallest integer such that its absmax is at most 448 * 2^k (within
+    [-127, 127]), codes E4M3(fl32(x_hat * 2^-k)) -- the FP8 operand of the
+    weight-gradient GEMM, in the layout of the 128x1 FP8 quantiser.
+
+    packed [rows, 1.5 cols] with chunk-major scales s [cols / 128, rows] as
+    `cache_1x128` writes them (rows a multiple of 128). Returns qT uint8
+    [cols, rows] and sT float32 [rows / 128, cols] (chunk-major, like the
+    library's 128x1 quantiser)."""
+    from oracle import e4m3, quant
+    rows = packed.shape[0]
+    assert rows % 128 == 0 and cols % 128 == 0
+    xh = uncache_1x128(packed, s, cols)                               # exact
+    g = np.ascontiguousarray(xh.T).reshape(cols, rows // 128, 128)
+    k = quant.pow2_exponent(np.max(np.abs(g), axis=-1))
+    v = (g * np.ldexp(1.0, -k)[..., None]).astype(np.float32)       # exact product, one fp32 rounding
+    qt = e4m3.encode(v).reshape(cols, rows)
+    st = np.ldexp(np.float32(1.0), k.astype(np.int32)).astype(np.float32).T.copy()
+    return qt, st

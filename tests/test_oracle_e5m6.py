@@ -129,3 +129,31 @@ def test_cache_of_exact_values_is_lossless():
     x = f32_to_bf16_bits(xf.astype(np.float32))
     packed, s = e5m6.cache_1x128(x)
     np.testing.assert_array_equal(e5m6.uncache_1x128(packed, s, 256), quant.bf16_bits_to_f32(x).astype(np.float64))
+
+
+def test_requant_equals_128x1_pow2_quantisation_of_the_cached_values():
+    # the cached values have at most 7 significant bits and lie in bf16's normal
+    # range here, so they are exact bf16 values; the 128x1 power-of-two FP8
+    # quantiser of those (a separately pinned function) must give the same codes
+    x = act(65, 256, 384, dist="student_t3", outlier_p=0.01, outlier_mult=50)
+    packed, s = e5m6.cache_1x128(x)
+    qt, st = e5m6.requant_128x1(packed, s, 384)
+    xh = e5m6.uncache_1x128(packed, s, 384)
+    xb = f32_to_bf16_bits(xh.astype(np.float32))
+    np.testing.assert_array_equal(quant.bf16_bits_to_f32(xb).astype(np.float64), xh)    # exact in bf16
+    qt2, st2 = quant.quant_act_128x1(xb, scale_mode="pow2")
+    np.testing.assert_array_equal(qt, qt2)
+    np.testing.assert_array_equal(st.T, st2)
+
+
+def test_requant_hand_worked_column():
+    # one column whose cached values are 3, -1.5, 0.25 and zeros: absmax 3 needs
+    # k = -7 (448 * 2^-8 = 1.75 < 3 <= 3.5), so the codes are E4M3(384) = 0x7C,
+    # E4M3(-192) = 0xF4 and E4M3(32) = 0x60 (exponent field 5 + 7 = 12, mantissa 0)
+    x = np.zeros((128, 128), np.float32)
+    x[0, 5], x[1, 5], x[2, 5] = 3.0, -1.5, 0.25
+    x[:, 0] = 1.0                                  # keeps the row tiles' scales ordinary
+    packed, s = e5m6.cache_1x128(f32_to_bf16_bits(x))
+    qt, st = e5m6.requant_128x1(packed, s, 128)
+    assert st[0, 5] == 2.0 ** -7
+    assert list(qt[5, :3]) == [0x7C, 0xF4, 0x60] and np.all(qt[5, 3:] == 0)
