@@ -146,6 +146,10 @@ def status_table(path):
                      f"cache {g['cache_us']:.1f} µs cold, {g['cache_GBps'] / 1000:.2f} TB/s = {pct(g['cache_frac_hbm'])}"
                      f" of 8 TB/s; read back {g['read_back_us']:.1f} µs, {g['read_back_GBps'] / 1000:.2f} TB/s = "
                      f"{pct(g['read_back_frac_hbm'])}"))
+        if "to_128x1_us" in g:
+            rows.append(("A11 E5M6 cache → 128×1 FP8 tiles (backward operand), X [16384, 7168]", g["to_128x1_kernel"],
+                         f"{g['to_128x1_us']:.1f} µs cold, {g['to_128x1_GBps'] / 1000:.2f} TB/s = "
+                         f"{pct(g['to_128x1_frac_hbm'])} of 8 TB/s"))
     if "pow2_scales" in v:
         g = v["pow2_scales"]
         rows.append(("NEXT-2 power-of-two scales (large fprop)", g["kernel"],
@@ -172,7 +176,7 @@ def status_table(path):
 
 # kernels that --leg launches alone (each on the workload the bench times it on)
 LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "mfma_stream",
-        "cache_e5m6", "uncache_e5m6")
+        "cache_e5m6", "uncache_e5m6", "requant_e5m6")
 
 
 def run_leg(args):
@@ -191,14 +195,14 @@ def run_leg(args):
     torch.cuda.set_device(0)
     sp = torch.cuda.current_stream(dev).cuda_stream
     leg = args.leg
-    cold = leg in ("quant_x", "quant_w", "qcol", "decode", "cache_e5m6", "uncache_e5m6")
+    cold = leg in ("quant_x", "quant_w", "qcol", "decode", "cache_e5m6", "uncache_e5m6", "requant_e5m6")
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
     flops = nbytes = None
 
     def dev16(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
 
-    if leg in ("cache_e5m6", "uncache_e5m6"):
+    if leg in ("cache_e5m6", "uncache_e5m6", "requant_e5m6"):
         cfg = workloads.large_fprop()
         _, M, _, K = WORKLOADS["large"]
         x = dev16(cfg.x)
@@ -213,11 +217,21 @@ def run_leg(args):
 
         def uncache():
             fb.fp8bq_uncache_e5m6_1x128(xe.data_ptr(), M, K, ldq_e, xes.data_ptr(), M, yb.data_ptr(), K, sp)
+
+        def requant():
+            fb.fp8bq_requant_e5m6_t_128x1(xe.data_ptr(), M, K, ldq_e, xes.data_ptr(), M, xet.data_ptr(), M,
+                                          xets.data_ptr(), K, sp)
         if leg == "cache_e5m6":
             fn = cache
-        else:
+        elif leg == "uncache_e5m6":
             cache()
             fn = uncache
+        else:
+            xet = torch.empty((K, M), dtype=torch.uint8, device=dev)
+            xets = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+            nbytes = M * (K * 3 // 2) + M * (K // 128) * 4 + K * M + (M // 128) * K * 4
+            cache()
+            fn = requant
     elif leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
         cfg = workloads.large_fprop()
         _, M, N, K = WORKLOADS["large"]
@@ -618,7 +632,20 @@ def main():
     bytes_e5m6 = M * K * 2 + M * nb_e + M * (K // 128) * 4
     log(f"[bench] E5M6 cache {st_t_ce['mean']:.1f} us, read back {st_t_ue['mean']:.1f} us "
         f"({bytes_e5m6 / st_t_ce['mean'] / 1e3:.0f} / {bytes_e5m6 / st_t_ue['mean'] / 1e3:.0f} GB/s)")
-    del xe, xes
+    # the backward use of the E5M6 cache: 128x1 FP8 tiles (power-of-two scales), transposed
+    xet = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    xets = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+
+    def requant_e5m6():
+        fb.fp8bq_requant_e5m6_t_128x1(xe.data_ptr(), M, K, ldq_e, xes.data_ptr(), M, xet.data_ptr(), M,
+                                      xets.data_ptr(), K, sp)
+
+    cache_e5m6()
+    requant_e5m6()
+    st_t_re = time_kernel(requant_e5m6, args.kernel_reps, True)
+    bytes_re = M * nb_e + M * (K // 128) * 4 + K * M + (M // 128) * K * 4
+    log(f"[bench] E5M6 cache -> 128x1 FP8: {st_t_re['mean']:.1f} us ({bytes_re / st_t_re['mean'] / 1e3:.0f} GB/s)")
+    del xe, xes, xet, xets
 
     # producer fusion: the GEMM quantises its own output (1x128 tiles) for the
     # next GEMM, against the GEMM followed by the quantiser of its bf16 output
@@ -1004,6 +1031,11 @@ def main():
                 "read_back_frac_hbm": round(bytes_e5m6 / st_t_ue["mean"] / 1e3 / PEAK_HBM_GBS, 4),
                 "algorithmic_bytes": bytes_e5m6,
                 "kernel": "cache_e5m6_kernel / uncache_e5m6_kernel",
+                "to_128x1_us": round(st_t_re["mean"], 2), "to_128x1_us_stats": rnd(st_t_re),
+                "to_128x1_GBps": round(bytes_re / st_t_re["mean"] / 1e3, 1),
+                "to_128x1_frac_hbm": round(bytes_re / st_t_re["mean"] / 1e3 / PEAK_HBM_GBS, 4),
+                "to_128x1_algorithmic_bytes": bytes_re,
+                "to_128x1_kernel": "requant_e5m6_t_kernel",
             },
             "decode_grouped": {
                 "what": f"{dec.name}: rows per expert {[int(c) for c in dec.real_rows]} (unpadded), "

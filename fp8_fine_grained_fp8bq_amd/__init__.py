@@ -11,11 +11,11 @@ Two layers with the C names:
 * `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
   `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`,
   `fp8bq_grouped_gemm_decode`, `fp8bq_cache_e5m6_1x128`,
-  `fp8bq_uncache_e5m6_1x128`: pointer-level, exactly the C signatures (ints
+  `fp8bq_uncache_e5m6_1x128`, `fp8bq_requant_e5m6_t_128x1`: pointer-level, exactly the C signatures (ints
   for pointers and the stream); a non-zero status raises `Fp8bqError`.
 * `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
   `gemm_quant`, `grouped_gemm`, `grouped_gemm_decode`, `cache_e5m6_1x128`,
-  `uncache_e5m6_1x128`: take torch tensors on
+  `uncache_e5m6_1x128`, `requant_e5m6_t_128x1`: take torch tensors on
   the GPU, allocate the outputs with torch (memory and streams are the only
   things torch provides) and call the same entry points on the current stream.
 """
@@ -36,7 +36,7 @@ SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flag
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
            "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_cache_e5m6_1x128",
-           "fp8bq_uncache_e5m6_1x128", "fp8bq_last_error", "fp8bq_version")
+           "fp8bq_uncache_e5m6_1x128", "fp8bq_requant_e5m6_t_128x1", "fp8bq_last_error", "fp8bq_version")
 
 
 class Fp8bqError(RuntimeError):
@@ -62,13 +62,15 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_requant_t_128x1.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, fp, i64, i32, vp]
         L.fp8bq_cache_e5m6_1x128.argtypes = [vp, i64, i64, i64, vp, i64, fp, i64, vp]
         L.fp8bq_uncache_e5m6_1x128.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, vp]
+        L.fp8bq_requant_e5m6_t_128x1.argtypes = [vp, i64, i64, i64, fp, i64, vp, i64, fp, i64, vp]
         L.fp8bq_gemm.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp]
         L.fp8bq_gemm_quant.argtypes = [i32, i64, i64, i64, vp, i64, fp, i64, vp, i64, fp, i64, vp, i64,
                                        vp, i64, fp, i64, i32, vp]
         L.fp8bq_grouped_gemm.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
                                          vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, i32, vp]
         for f in ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-                  "fp8bq_grouped_gemm", "fp8bq_cache_e5m6_1x128", "fp8bq_uncache_e5m6_1x128"):
+                  "fp8bq_grouped_gemm", "fp8bq_cache_e5m6_1x128", "fp8bq_uncache_e5m6_1x128",
+                  "fp8bq_requant_e5m6_t_128x1"):
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
         L.fp8bq_grouped_gemm_decode.argtypes = L.fp8bq_grouped_gemm.argtypes
@@ -197,6 +199,11 @@ def fp8bq_uncache_e5m6_1x128(q, rows, cols, ldq, s, lds, y, ldy, stream=0):
                   lib().fp8bq_uncache_e5m6_1x128(q, rows, cols, ldq, s, lds, y, ldy, stream))
 
 
+def fp8bq_requant_e5m6_t_128x1(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, stream=0):
+    return _check("fp8bq_requant_e5m6_t_128x1",
+                  lib().fp8bq_requant_e5m6_t_128x1(q, rows, cols, ldq, s, lds, qt, ldqt, st, ldst, stream))
+
+
 def cache_e5m6_1x128(x):
     """bf16 [rows, cols] (int16/bfloat16 storage) -> (q uint8 [rows, 1.5 cols]: packed 12-bit E5M6
     codes, s float32 [cols/128, rows]: chunk-major power-of-two 1x128 tile scales)."""
@@ -222,6 +229,23 @@ def uncache_e5m6_1x128(q, s, cols):
     fp8bq_uncache_e5m6_1x128(q.data_ptr(), rows, cols, q.stride(0), s.data_ptr(), s.stride(0), y.data_ptr(), cols,
                              _stream(q))
     return y
+
+
+def requant_e5m6_t_128x1(q, s, cols):
+    """E5M6 cache q (rows of >= 1.5 cols bytes, row stride q.stride(0)) with its power-of-two
+    scales s [cols/128, >=rows] -> (qt uint8 [cols, rows], st float32 [rows/128, cols]): the cached
+    values re-quantised to E4M3 in 128x1 tiles with power-of-two scales, COLWISE layout."""
+    import torch
+    if q.dtype != torch.uint8 or q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError("q must be a 2-D row-major uint8 tensor")
+    if s.dtype != torch.float32 or s.dim() != 2 or s.stride(1) != 1:
+        raise ValueError("s must be a 2-D row-major float32 tensor")
+    rows = q.shape[0]
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=q.device)
+    st = torch.empty((rows // 128, cols), dtype=torch.float32, device=q.device)
+    fp8bq_requant_e5m6_t_128x1(q.data_ptr(), rows, cols, q.stride(0), s.data_ptr(), s.stride(0), qt.data_ptr(),
+                               rows, st.data_ptr(), cols, _stream(q))
+    return qt, st
 
 
 def requant_t_128x1(q, s):

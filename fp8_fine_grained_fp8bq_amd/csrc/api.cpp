@@ -139,6 +139,26 @@ int fp8bq_uncache_e5m6_1x128(const void* q, int64_t rows, int64_t cols, int64_t 
                   "uncache_e5m6");
 }
 
+int fp8bq_requant_e5m6_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
+                                void* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+  if (!q || !s || !qt || !st) return fail(FP8BQ_E_INVAL, "requant_e5m6_t: null pointer");
+  if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "requant_e5m6_t: rows and cols must be positive");
+  if (rows % 128 || cols % 128)
+    return fail(FP8BQ_E_SHAPE, "requant_e5m6_t: rows (%lld) and cols (%lld) must be multiples of 128", (long long)rows,
+                (long long)cols);
+  if (ldq / 3 < cols / 2) return fail(FP8BQ_E_INVAL, "requant_e5m6_t: ldq (bytes) < 1.5 * cols");
+  if (ldqt < rows) return fail(FP8BQ_E_INVAL, "requant_e5m6_t: ldqt must be >= rows");
+  if (lds < rows || ldst < cols) return fail(FP8BQ_E_INVAL, "requant_e5m6_t: lds must be >= rows and ldst >= cols");
+  if (cols / 128 > 65535 || rows / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "requant_e5m6_t: too large");
+  if (!aligned(q, 16) || !aligned(qt, 16) || !aligned(s, 4) || !aligned(st, 4))
+    return fail(FP8BQ_E_ALIGN, "requant_e5m6_t: q and qt must be 16-byte aligned, scales 4-byte aligned");
+  if (ldq % 16 || ldqt % 16) return fail(FP8BQ_E_ALIGN, "requant_e5m6_t: ldq and ldqt must be multiples of 16");
+  if (int stt = check_device()) return stt;
+  return launched(fp8bq::launch_requant_e5m6_t(static_cast<const uint8_t*>(q), rows, cols, ldq, s, lds,
+                                               static_cast<uint8_t*>(qt), ldqt, st, ldst,
+                                               reinterpret_cast<hipStream_t>(stream)), "requant_e5m6_t");
+}
+
 int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
                           void* qt, int64_t ldqt, float* st, int64_t ldst, int flags, void* stream) {
   if (!q || !s || !qt || !st) return fail(FP8BQ_E_INVAL, "requant_t: null pointer");

@@ -26,6 +26,9 @@ hipError_t launch_cache_e5m6(const uint16_t* x, int64_t rows, int64_t cols, int6
                              float* s, int64_t lds, hipStream_t st);
 hipError_t launch_uncache_e5m6(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
                                int64_t lds, uint16_t* y, int64_t ldy, hipStream_t st);
+// E5M6 cache -> transposed 128x1 FP8 tiles with power-of-two scales.
+hipError_t launch_requant_e5m6_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                                  int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream);
 
 enum GemmKind { KIND_FPROP = 0, KIND_DGRAD = 1, KIND_WGRAD = 2 };
 

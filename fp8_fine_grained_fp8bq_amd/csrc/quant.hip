@@ -519,6 +519,116 @@ __global__ __launch_bounds__(kRowThreads) void uncache_e5m6_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// E5M6 cache -> 128x1 FP8 tiles (the backward use of the cache: its 1x128
+// tiles become the 128x1 tiles of the weight-gradient operand). x_hat =
+// E5M6(code) * 2^kc exactly; per 128 rows of one column, k = the smallest
+// integer with absmax <= 448 * 2^k (within [-127, 127]) and codes
+// E4M3(fl32(x_hat * 2^-k)); the output scale is 2^k.
+//
+// All in fp32. A code shifted left by 4 is the IEEE binary16 pattern of its
+// value, so one half-to-float conversion decodes it (exactly, subnormals
+// included). y = value * 2^(kc - 2) is exact: y has at most 7 significant
+// bits, its smallest possible quantum is 2^-20 * 2^-127 * 2^-2 = 2^-149 and its
+// magnitude stays below 2^16 * 2^113 * 2^-2 = 2^127 (a bf16 input keeps kc <=
+// 113; the 2^-2 is what keeps the largest cached value, up to 2^128, finite).
+// The column absmax is then a plain fp32 max over y, and the code input is
+// ldexp(y, 2 - k): exact unless it falls below 2^-126, where every value
+// encodes to a signed E4M3 zero anyway.
+//
+// One 256-thread block per 128 x 128 block of values (a 128-row x 192-byte
+// piece of the cache). Staging: 16 lanes per row, each loading 12 bytes (8
+// codes) and storing them as 8 binary16 patterns (16 bytes) to LDS. Then
+// thread (p, seg) takes columns 4p .. 4p + 3 of rows 16 seg .. 16 seg + 15,
+// as in the FP8 re-quantisation above.
+// LDS tile: row r at 256 r bytes; the 8-byte unit u (codes 4u .. 4u + 3) sits
+// at unit u ^ e5_swz(r >> 4). Over any 16 lanes of a read (p in {2i, 2i+1},
+// seg 0..7) the units are 16 distinct ones of 16 consecutive aligned units,
+// and over 32 lanes 32 distinct units: every read is free of bank conflicts.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e5_swz(int seg) { return (seg << 1) ^ ((seg & 1) << 4); }
+
+// Smallest k with a <= 448 * 2^k from y = a / 4 (a >= 0, y exact), within
+// [-127, 127]. y = f * 2^(E - 127): k = E - 133, plus one when f > 1.75.
+__device__ __forceinline__ int pow2_exponent_y4(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const int k = (int)(b >> 23) - 133 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(-127, min(127, k));
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+__global__ __launch_bounds__(256) void requant_e5m6_t_kernel(
+    const uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
+  __shared__ uint4 tile[128 * 16];   // 128 rows x 16 units of 16 bytes
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 128, c0 = (int64_t)blockIdx.y * 128;
+  const int l16 = t & 15, rs = t >> 4;
+
+  uint3 in[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    in[j] = *reinterpret_cast<const uint3*>(q + (r0 + 16 * j + rs) * ldq + blockIdx.y * 192 + l16 * 12);
+  const int p = t >> 3, seg = t & 7;
+  float sc[16];   // 2^(kc - 2) of the 16 rows (exact: the cache scales are powers of two)
+  const float* srow = s + (int64_t)blockIdx.y * lds + r0 + seg * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] = srow[i] * 0.25f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint3 v = in[j];
+    const uint32_t pr[4] = {v.x & 0xFFFFFFu, (v.x >> 24) | ((v.y & 0xFFFFu) << 8),
+                            (v.y >> 16) | ((v.z & 0xFFu) << 16), v.z >> 8};
+    uint32_t h[4];   // codes 2i, 2i + 1 as binary16 patterns (code << 4) in the low / high half
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = ((pr[i] << 4) & 0xFFF0u) | ((pr[i] << 8) & 0xFFF00000u);
+    // row 16 j + rs, units 2 l16 and 2 l16 + 1 -> 16-byte slot l16 ^ (e5_swz(j) / 2)
+    tile[(16 * j + rs) * 16 + (l16 ^ (e5_swz(j) >> 1))] = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+  __syncthreads();
+
+  const uint2* lt = reinterpret_cast<const uint2*>(tile);
+  float y[16][4];
+  float cmax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint2 w = lt[(seg * 16 + i) * 32 + (p ^ e5_swz(seg))];
+    y[i][0] = half_lo(w.x) * sc[i];
+    y[i][1] = half_hi(w.x) * sc[i];
+    y[i][2] = half_lo(w.y) * sc[i];
+    y[i][3] = half_hi(w.y) * sc[i];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) cmax[b] = fmaxf(cmax[b], fabsf(y[i][b]));
+  }
+  int k[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) k[b] = pow2_exponent_y4(__uint_as_float(lane8_max(__float_as_uint(cmax[b]))));
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n = 2 - k[b];
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_ldexpf(y[i][b], n);
+    uint4 o;
+    o.x = cvt4(v[0], v[1], v[2], v[3]);
+    o.y = cvt4(v[4], v[5], v[6], v[7]);
+    o.z = cvt4(v[8], v[9], v[10], v[11]);
+    o.w = cvt4(v[12], v[13], v[14], v[15]);
+    *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldqt + r0 + seg * 16) = o;
+  }
+  if (seg == 0) {
+    float* sp = st + (int64_t)blockIdx.x * ldst + c0 + 4 * p;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sp[b] = exp2_int(k[b]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -546,6 +656,13 @@ hipError_t launch_requant_t(const uint8_t* q, int64_t rows, int64_t cols, int64_
                             int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream) {
   dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 128));
   hipLaunchKernelGGL(requant_t_kernel, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_e5m6_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                                  int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream) {
+  dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 128));
+  hipLaunchKernelGGL(requant_e5m6_t_kernel, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
   return hipGetLastError();
 }
 

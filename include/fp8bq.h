@@ -141,6 +141,37 @@ int fp8bq_uncache_e5m6_1x128(const void* q, int64_t rows, int64_t cols, int64_t 
                              const float* s, int64_t lds, void* y, int64_t ldy, void* stream);
 
 /*
+ * The backward use of the E5M6 cache (report section 3.3.3, low-precision
+ * activations, item 1: the cached 1x128 tiles are turned into 128x1 tiles for
+ * the backward pass, and with power-of-two scales the conversion itself adds
+ * no quantisation error): the cached values x_hat = E5M6(code) * s, exact, are
+ * re-quantised to E4M3 in 128x1 tiles (128 consecutive rows of one column) and
+ * written transposed, ready to be the activation operand of the Wgrad GEMM.
+ *
+ * q, ldq, s, lds  as written by fp8bq_cache_e5m6_1x128: s must hold powers of
+ *       two 2^kc with -127 <= kc <= 113 (the range the cache writes for finite
+ *       bf16 input; only the exponent is read) and codes must be finite
+ *       (exponent field below 31). The values are then formed exactly in fp32
+ *       as E5M6(code) * 2^(kc - 2), which stays within [2^-149, 2^127).
+ * qt    E4M3 [cols, rows], ldqt >= rows: qt[j * ldqt + r] encodes column j,
+ *       row r (the layout fp8bq_quant_act_1x128 writes in COLWISE mode).
+ * st    float, scale of tile (rows [128c, 128c+128), column j) at
+ *       st[c * ldst + j], ldst >= cols: 2^k with k the smallest integer such
+ *       that the tile's absmax <= 448 * 2^k, within [-127, 127] (2^-127 for
+ *       an all-zero tile); codes E4M3(fl32(x_hat * 2^-k)), nearest even, sign
+ *       kept. With x_hat in bf16's normal range this is bit for bit
+ *       fp8bq_quant_act_1x128 (COLWISE | FP8BQ_SCALE_POW2) of the bf16 values
+ *       that fp8bq_uncache_e5m6_1x128 returns.
+ * rows and cols must be multiples of 128. The caller owns all buffers; the
+ * inputs must not overlap the outputs.
+ * Errors: E_INVAL (null, sizes <= 0, ld too small), E_SHAPE, E_ALIGN (q, qt
+ *         16-byte aligned; ldq, ldqt multiples of 16; scales 4-byte aligned),
+ *         E_DEVICE, E_HIP.
+ */
+int fp8bq_requant_e5m6_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
+                               int64_t lds, void* qt, int64_t ldqt, float* st, int64_t ldst, void* stream);
+
+/*
  * Transposing re-quantisation of an FP8 activation cache, 1x128 -> 128x1
  * (report section 3.5.2 "support for transposed GEMM": the forward pass keeps
  * activations as 1x128 FP8 tiles, the backward pass reads them, dequantises,

@@ -65,6 +65,12 @@ hipError_t launch_uncache_e5m6(const uint8_t*, int64_t rows, int64_t cols, int64
   if (rows <= 0 || cols % 128 || ldy < cols || ldq < cols / 2 * 3 || lds < rows) std::abort();
   return LAUNCHED();
 }
+hipError_t launch_requant_e5m6_t(const uint8_t*, int64_t rows, int64_t cols, int64_t ldq, const float*, int64_t lds,
+                                  uint8_t*, int64_t ldqt, float*, int64_t ldst, hipStream_t) {
+  if (rows <= 0 || rows % 128 || cols % 128 || ldq < cols / 2 * 3 || ldqt < rows || lds < rows || ldst < cols)
+    std::abort();
+  return LAUNCHED();
+}
 hipError_t launch_gemm(int kind, int64_t, int64_t n, int64_t k, const uint8_t*, int64_t, const float*, int64_t,
                        const uint8_t*, int64_t, const float*, int64_t, void*, int64_t, bool, hipStream_t) {
   if (kind < 0 || kind > 2 || n % 128 || k % 128) std::abort();
@@ -153,6 +159,32 @@ static void validation() {
     EXPECT(fp8bq_uncache_e5m6_1x128(P(B16), 1024, INT64_MAX / 3 / 128 * 128, INT64_MAX / 16 * 16, F(S4), 1024,
                                     P(A16), INT64_MAX / 8 * 8, nullptr), FP8BQ_E_SHAPE);
   }
+  // fp8bq_requant_e5m6_t_128x1
+  EXPECT(fp8bq_requant_e5m6_t_128x1(nullptr, 256, 384, 576, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 200, 384, 576, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_SHAPE);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 560, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 576, F(S4), 255, P(B16), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 576, F(S4), 256, P(B16), 256, F(S4 + 4096), 383, nullptr),
+         FP8BQ_E_INVAL);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 584, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_ALIGN);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 576, F(S4), 256, P(B16 + 4), 256, F(S4 + 4096), 384, nullptr),
+         FP8BQ_E_ALIGN);
+  {
+    const int64_t huge = INT64_MAX / 128 * 128;
+    // 1.5 * cols past INT64_MAX: rejected on ldq without forming the product
+    EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 128, huge, INT64_MAX / 16 * 16, F(S4), 128, P(B16), 128, F(S4),
+                                      huge, nullptr), FP8BQ_E_INVAL);
+    // row or column blocks past the grid
+    EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), huge, 128, 192, F(S4), huge, P(B16), huge, F(S4), 128, nullptr),
+           FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 128, 128 * 65536, 192 * 65536, F(S4), 128, P(B16), 128, F(S4),
+                                      128 * 65536, nullptr), FP8BQ_E_SHAPE);
+  }
   // fp8bq_requant_t_128x1
   EXPECT(fp8bq_requant_t_128x1(nullptr, 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_INVAL);
   EXPECT(fp8bq_requant_t_128x1(P(A16), 200, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), FP8BQ_E_SHAPE);
@@ -219,6 +251,7 @@ static void accepted(int want) {
   EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), want);
   EXPECT(fp8bq_cache_e5m6_1x128(P(A16), 100, 384, 384, P(B16), 576, F(S4), 100, nullptr), want);
   EXPECT(fp8bq_uncache_e5m6_1x128(P(B16), 100, 384, 576, F(S4), 100, P(A16), 384, nullptr), want);
+  EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 576, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr), want);
   for (int op = 0; op < 3; ++op) {
     const int64_t ldsb = op == 0 ? 8 : op == 1 ? 3 : 384;
     EXPECT(fp8bq_gemm(op, 300, 384, 1024, P(A16), 1024, F(S4), 300, P(B16), 1024, F(S4), ldsb, P(O16), 384, nullptr), want);

@@ -110,6 +110,32 @@ def test_requant_validation(L):
     assert "too large" in L.fp8bq_last_error().decode()
 
 
+def test_requant_e5m6_validation(L):
+    f = "fp8bq_requant_e5m6_t_128x1"
+    # rows, cols = 256, 384: packed codes 576 bytes per row, s lds 256, qt [384, 256] ldqt 256, st ldst 384
+    ok = [A16, 256, 384, 576, S4, 256, B16, 256, S4 + 4096, 384, None]
+    def bad(i, v):
+        a = list(ok); a[i] = v
+        return _st(L, f, *a)
+    assert _st(L, f, *ok) == fb.E_DEVICE
+    assert bad(0, None) == fb.E_INVAL and bad(8, None) == fb.E_INVAL
+    assert bad(1, 0) == fb.E_INVAL
+    assert bad(1, 200) == fb.E_SHAPE                                            # rows % 128
+    assert bad(2, 300) == fb.E_SHAPE                                            # cols % 128
+    assert bad(3, 560) == fb.E_INVAL                                            # ldq < 1.5 cols
+    assert bad(5, 255) == fb.E_INVAL                                            # lds < rows
+    assert bad(7, 128) == fb.E_INVAL                                            # ldqt < rows
+    assert bad(9, 383) == fb.E_INVAL                                            # ldst < cols
+    assert bad(0, A16 + 4) == fb.E_ALIGN
+    assert bad(6, B16 + 8) == fb.E_ALIGN
+    assert bad(3, 584) == fb.E_ALIGN                                            # ldq % 16
+    assert bad(7, 264) == fb.E_ALIGN                                            # ldqt % 16
+    assert bad(4, S4 + 2) == fb.E_ALIGN
+    wide = 128 * 65536                                                          # 65536 column blocks: one past the grid
+    assert _st(L, f, A16, 128, wide, 192 * 65536, S4, 128, B16, 128, S4, wide, None) == fb.E_SHAPE
+    assert "too large" in L.fp8bq_last_error().decode()
+
+
 @pytest.mark.parametrize("f", ["fp8bq_cache_e5m6_1x128", "fp8bq_uncache_e5m6_1x128"])
 def test_e5m6_validation(L, f):
     # rows, cols = 100, 384: bf16 [100, 384] ld 384; packed codes 576 bytes per row, ldq 576; s lds 100
