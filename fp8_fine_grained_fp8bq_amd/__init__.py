@@ -10,7 +10,8 @@ Two layers with the C names:
 
 * `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
   `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`,
-  `fp8bq_grouped_gemm_decode`, `fp8bq_cache_e5m6_1x128`,
+  `fp8bq_grouped_gemm_decode`, `fp8bq_grouped_gemm_decode_workspace_size`,
+  `fp8bq_grouped_gemm_decode_ws`, `fp8bq_cache_e5m6_1x128`,
   `fp8bq_uncache_e5m6_1x128`, `fp8bq_requant_e5m6_t_128x1`: pointer-level, exactly the C signatures (ints
   for pointers and the stream); a non-zero status raises `Fp8bqError`.
 * `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
@@ -35,7 +36,8 @@ ACT_ROWWISE, ACT_COLWISE = 0, 1
 SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flags` elsewhere)
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
-           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode", "fp8bq_cache_e5m6_1x128",
+           "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode",
+           "fp8bq_grouped_gemm_decode_workspace_size", "fp8bq_grouped_gemm_decode_ws", "fp8bq_cache_e5m6_1x128",
            "fp8bq_uncache_e5m6_1x128", "fp8bq_requant_e5m6_t_128x1", "fp8bq_last_error", "fp8bq_version")
 
 
@@ -74,6 +76,12 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = ctypes.c_int
         L.fp8bq_last_error.restype = ctypes.c_char_p
         L.fp8bq_grouped_gemm_decode.argtypes = L.fp8bq_grouped_gemm.argtypes
+        L.fp8bq_grouped_gemm_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64,
+                                                               i64, ctypes.POINTER(ctypes.c_int64)]
+        L.fp8bq_grouped_gemm_decode_workspace_size.restype = ctypes.c_int
+        L.fp8bq_grouped_gemm_decode_ws.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
+                                                   vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp, i64, i32, vp]
+        L.fp8bq_grouped_gemm_decode_ws.restype = ctypes.c_int
         L.fp8bq_last_error.argtypes = []
         L.fp8bq_version.restype = ctypes.c_char_p
         L.fp8bq_version.argtypes = []
@@ -313,16 +321,63 @@ def grouped_gemm(row_off, a, sa, b, sb, out=None, pow2: bool = False):
     return out
 
 
-def grouped_gemm_decode(row_off, a, sa, b, sb, out=None):
+def _offsets(groups, row_off):
+    return (ctypes.c_int64 * (groups + 1))(*[int(v) for v in row_off]) if row_off is not None else None
+
+
+def fp8bq_grouped_gemm_decode_workspace_size(groups, row_off, n, k):
+    """Bytes of workspace fp8bq_grouped_gemm_decode_ws needs (row_off: host sequence)."""
+    out = ctypes.c_int64(-1)
+    _check("fp8bq_grouped_gemm_decode_workspace_size",
+           lib().fp8bq_grouped_gemm_decode_workspace_size(groups, _offsets(groups, row_off), n, k, ctypes.byref(out)))
+    return out.value
+
+
+def fp8bq_grouped_gemm_decode_ws(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, workspace,
+                                 workspace_bytes, flags=0, stream=0):
+    return _check("fp8bq_grouped_gemm_decode_ws",
+                  lib().fp8bq_grouped_gemm_decode_ws(groups, _offsets(groups, row_off), n, k, a, lda, sa, ldsa, b,
+                                                     ldb, sb, ldsb, out, ldo, workspace, workspace_bytes, flags,
+                                                     stream))
+
+
+_workspaces = {}
+
+
+def decode_workspace(nbytes, device):
+    """A zero-filled device workspace of at least nbytes for fp8bq_grouped_gemm_decode_ws, kept
+    per device and reused (every call leaves its counters zero). Calls that share it must run
+    on one stream."""
+    import torch
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def grouped_gemm_decode(row_off, a, sa, b, sb, out=None, split=True):
     """Decode-shape grouped Fprop: row_off host sequence of G + 1 offsets (any counts up to
     256 rows per expert); a uint8 [m, k]; sa [k/128, >=m]; b uint8 [G, n, k];
-    sb float32 [G, n/128, k/128]. Returns bf16 [m, n]."""
+    sb float32 [G, n/128, k/128]. Returns bf16 [m, n]. split: experts of more than 32 rows
+    run as 128-column half-K workgroup pairs through a cached workspace."""
     import torch
     G, n, k = b.shape
     m = a.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if split:
+        need = fp8bq_grouped_gemm_decode_workspace_size(G, list(row_off), n, k)
+        ws = decode_workspace(need, a.device) if need > 0 else None
+        fp8bq_grouped_gemm_decode_ws(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
+                                     b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
+                                     out.stride(0), ws.data_ptr() if ws is not None else None,
+                                     ws.numel() if ws is not None else 0, 0, _stream(a))
+        return out
     fp8bq_grouped_gemm_decode(G, list(row_off), n, k, a.data_ptr(), a.stride(0), sa.data_ptr(), sa.stride(0),
                               b.data_ptr(), b.stride(1), sb.data_ptr(), sb.stride(1), out.data_ptr(),
                               out.stride(0), 0, _stream(a))
     return out
+
+

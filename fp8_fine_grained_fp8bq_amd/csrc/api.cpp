@@ -299,34 +299,83 @@ int fp8bq_grouped_gemm(int32_t groups, const int64_t* row_off, int64_t n, int64_
                   "grouped_gemm");
 }
 
+// Offsets of a decode-shape launch: G in range, row_off[0] == 0,
+// non-decreasing, at most kMaxDecodeRows rows per expert.
+static int check_decode_offsets(const char* who, int32_t groups, const int64_t* row_off) {
+  if (groups < 1 || groups > fp8bq::kMaxGroups)
+    return fail(FP8BQ_E_INVAL, "%s: groups must be in [1, %d], got %d", who, fp8bq::kMaxGroups, groups);
+  if (!row_off) return fail(FP8BQ_E_INVAL, "%s: null row_off", who);
+  if (row_off[0] != 0) return fail(FP8BQ_E_SHAPE, "%s: row_off[0] must be 0", who);
+  for (int e = 0; e < groups; ++e) {
+    const int64_t rows = row_off[e + 1] - row_off[e];
+    if (rows < 0) return fail(FP8BQ_E_SHAPE, "%s: row_off must be non-decreasing (at %d)", who, e);
+    if (rows > fp8bq::kMaxDecodeRows)
+      return fail(FP8BQ_E_SHAPE, "%s: group %d has %lld rows, at most %d", who, e, (long long)rows,
+                  fp8bq::kMaxDecodeRows);
+  }
+  return FP8BQ_OK;
+}
+
+static int check_decode(const char* who, int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                        const void* a, int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
+                        const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags) {
+  if (flags != 0) return fail(FP8BQ_E_INVAL, "%s: flags must be 0, got %d", who, flags);
+  if (int st = check_decode_offsets(who, groups, row_off)) return st;
+  const int64_t m = row_off[groups];
+  if (int st = check_gemm_common(who, m > 0 ? m : 1, n, k, a, lda, sa, b, ldb, sb, out, ldo, 2)) return st;
+  if (product_at_least(groups, n / 64, (int64_t)1 << 31)) return fail(FP8BQ_E_SHAPE, "%s: too many column slices", who);
+  if (ldsa < m) return fail(FP8BQ_E_INVAL, "%s: ldsa must be >= m", who);
+  if (ldsb < k / 128) return fail(FP8BQ_E_INVAL, "%s: ldsb must be >= k / 128", who);
+  return FP8BQ_OK;
+}
+
 int fp8bq_grouped_gemm_decode(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
                               int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
                               const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags, void* stream) {
-  if (flags != 0) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: flags must be 0, got %d", flags);
-  if (groups < 1 || groups > fp8bq::kMaxGroups)
-    return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: groups must be in [1, %d], got %d", fp8bq::kMaxGroups, groups);
-  if (!row_off) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: null row_off");
-  if (row_off[0] != 0) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: row_off[0] must be 0");
-  for (int e = 0; e < groups; ++e) {
-    const int64_t rows = row_off[e + 1] - row_off[e];
-    if (rows < 0) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: row_off must be non-decreasing (at %d)", e);
-    if (rows > fp8bq::kMaxDecodeRows)
-      return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: group %d has %lld rows, at most %d", e, (long long)rows,
-                  fp8bq::kMaxDecodeRows);
-  }
-  const int64_t m = row_off[groups];
-  if (int st = check_gemm_common("grouped_gemm_decode", m > 0 ? m : 1, n, k, a, lda, sa, b, ldb, sb, out, ldo, 2))
+  if (int st = check_decode("grouped_gemm_decode", groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out,
+                            ldo, flags))
     return st;
-  if (product_at_least(groups, n / 64, (int64_t)1 << 31)) return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode: too many column slices");
-  if (ldsa < m) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsa must be >= m");
-  if (ldsb < k / 128) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode: ldsb must be >= k / 128");
   if (int st = check_device()) return st;
-  if (m == 0) return FP8BQ_OK;
+  if (row_off[groups] == 0) return FP8BQ_OK;
   return launched(fp8bq::launch_grouped_gemm_decode(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda, sa,
                                                     ldsa, static_cast<const uint8_t*>(b), ldb, sb, ldsb,
-                                                    static_cast<uint16_t*>(out), ldo,
+                                                    static_cast<uint16_t*>(out), ldo, nullptr,
                                                     reinterpret_cast<hipStream_t>(stream)),
                   "grouped_gemm_decode");
+}
+
+int fp8bq_grouped_gemm_decode_workspace_size(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                                             int64_t* bytes) {
+  if (!bytes) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode_workspace_size: null bytes");
+  if (int st = check_decode_offsets("grouped_gemm_decode_workspace_size", groups, row_off)) return st;
+  if (n <= 0 || k <= 0 || n % 128 || k % 128)
+    return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode_workspace_size: n and k must be positive multiples of 128");
+  if (product_at_least(groups, n / 64, (int64_t)1 << 31))
+    return fail(FP8BQ_E_SHAPE, "grouped_gemm_decode_workspace_size: too many column slices");
+  *bytes = fp8bq::grouped_gemm_decode_workspace(groups, row_off, n, k);
+  return FP8BQ_OK;
+}
+
+int fp8bq_grouped_gemm_decode_ws(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
+                                 int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
+                                 const float* sb, int64_t ldsb, void* out, int64_t ldo, void* workspace,
+                                 int64_t workspace_bytes, int flags, void* stream) {
+  if (int st = check_decode("grouped_gemm_decode_ws", groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out,
+                            ldo, flags))
+    return st;
+  const int64_t need = fp8bq::grouped_gemm_decode_workspace(groups, row_off, n, k);
+  if (need > 0 && !workspace) return fail(FP8BQ_E_INVAL, "grouped_gemm_decode_ws: null workspace (%lld bytes needed)", (long long)need);
+  if (need > 0 && workspace_bytes < need)
+    return fail(FP8BQ_E_INVAL, "grouped_gemm_decode_ws: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  if (need > 0 && !aligned(workspace, 16)) return fail(FP8BQ_E_ALIGN, "grouped_gemm_decode_ws: workspace must be 16-byte aligned");
+  if (int st = check_device()) return st;
+  if (row_off[groups] == 0) return FP8BQ_OK;
+  return launched(fp8bq::launch_grouped_gemm_decode(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda, sa,
+                                                    ldsa, static_cast<const uint8_t*>(b), ldb, sb, ldsb,
+                                                    static_cast<uint16_t*>(out), ldo, need > 0 ? workspace : nullptr,
+                                                    reinterpret_cast<hipStream_t>(stream)),
+                  "grouped_gemm_decode_ws");
 }
 
 }  // extern "C"

@@ -10,20 +10,31 @@
 // up to 256.
 //
 // Design (MI355X / gfx950):
-//  * One workgroup per (expert, 64 output columns), 8 waves (more waves issue
-//    the loads: each load instruction keeps its wave for a while). The
-//    expert's rows are T subtiles of 16 (T = 1, 2, 4, 8 or 16 for its count;
-//    the LDS allocation follows the launch's largest expert); wave w computes
-//    subtiles w, w + 8, ... against the slice's four weight subtiles, so
-//    every activation fragment is read from LDS once. 64 columns lie inside
-//    one 128 x 128 weight block, so a chunk has one weight scale per
-//    workgroup.
-//  * The weight slice streams through an LDS ring of kWStages chunks (8 KB
-//    each) with global -> LDS DMA, issued kWStages - 1 chunks ahead: that is
-//    the memory-level parallelism the HBM stream needs (≈ 40-64 KB in flight
-//    per CU). The expert's activation rows (read by every column slice, so
-//    mostly from L2) go through a shorter ring of kAStages chunks. Rows past
-//    the expert's end read as zeros (buffer bound) and are never stored.
+//  * Two workgroup shapes, each streaming 64 x K weight bytes: an expert of at
+//    most 32 rows gets one workgroup per 64 output columns over all of K; a
+//    larger expert (when the caller gives a workspace) one per 128 output
+//    columns and half of K. A workgroup moves its weight slice once and its
+//    expert's rows once per K range, so the 128-column shape reads half the
+//    activation bytes per output column. Per CU the bytes moved, not the
+//    matrix unit, set a workgroup's time: a 64-column workgroup of a 217-row
+//    expert moves 0.46 MB of weights and 1.6 MB of activations; its 128-column
+//    half-K pair 0.46 + 0.8 MB each. The two halves add their FP32 sums: each
+//    stores its partial sums with device-coherent stores and bumps a counter;
+//    the second to finish adds the other's partial (two-term sums are the
+//    same in either order) and writes the bf16 output. Nobody waits.
+//  * 8 waves (more waves issue the loads: each load instruction keeps its
+//    wave for a while). The expert's rows are T subtiles of 16, T the next
+//    available count at or above rows / 16 (1, 2, 3, 4, 6, 8, 10, 12, 14 or 16;
+//    rows past the expert's end read as zeros through the buffer bound and are
+//    never stored). 64-column shape: wave w computes row subtiles w, w + 8
+//    against the slice's four weight subtiles. 128-column shape: wave w
+//    computes the four weight subtiles of column half w % 2 against row
+//    subtiles w / 2, w / 2 + 4, ... Either way a 64 or 128 column slice lies
+//    inside one 128 x 128 weight block: a chunk has one weight scale.
+//  * The weight slice streams through an LDS ring of kWStages chunks with
+//    global -> LDS DMA (non-temporal: each weight byte is read once), issued
+//    kWStages - 1 chunks ahead; the activation rows (mostly L2 hits: every
+//    column slice of the expert reads them) through a ring of kAStages chunks.
 //  * One barrier per chunk; before it each wave waits only until its own DMA
 //    for the chunk has landed (vmcnt counted from the fixed issue pattern, with
 //    the final chunks re-issued so that the count stays exact). The loads are
@@ -40,7 +51,8 @@
 namespace fp8bq {
 namespace {
 
-constexpr int kDN = 64;   // output columns per workgroup
+constexpr int kDN = 64;    // output columns of a full-K workgroup
+constexpr int kDN2 = 128;  // output columns of a half-K workgroup
 
 // LDS DMA of one dword per lane through a raw buffer resource (see dma16_buf).
 __device__ __forceinline__ void dma4_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
@@ -58,41 +70,51 @@ __device__ __forceinline__ void dma16_buf_nt(const u32x4& rsrc, uint32_t voff, u
 }
 
 struct DecodeArgs {
-  int64_t n, k;
+  int64_t n, k, m;
   const uint8_t* a; int64_t lda;
   const float* sa; int64_t ldsa;
   const uint8_t* b; int64_t ldb;       // expert e's weight [n, k] at b + e * n * ldb
   const float* sb; int64_t ldsb;       // expert e's block grid at sb + e * (n / 128) * ldsb
   uint16_t* out; int64_t ldo;
-  int groups, slices;                  // slices = n / 64
+  float* part;                         // split experts' partial sums (layout at decode_slice's epilogue)
+  uint32_t* cnt;                       // counter of (expert e, 128-column slice s) at cnt[e * 256 + s]; zero between calls
+  int groups, slices;                  // slices = n / 64 workgroups per expert
+  int part_subtiles;                   // 16-row subtiles of all split experts (one K half's share of part)
   int row_off[kMaxGroups + 1];
+  int part_off[kMaxGroups];            // split expert e's first subtile in part
+  uint8_t split[kMaxGroups];           // 1: the expert runs as 128-column, half-K workgroups
 };
 
-template <int T>
+template <int T, int CW>
 struct DecodeCfg {
-  static constexpr int kAStages = T >= 16 ? 3 : 4;
-  static constexpr int kWStages = T >= 16 ? 5 : 8;
+  static_assert(CW == kDN || CW == kDN2, "workgroup width");
+  static constexpr bool kWide = CW == kDN2;
+  static constexpr int kAStages = T > 8 ? 3 : 4;
+  static constexpr int kWStages = kWide ? (T >= 15 ? 3 : T >= 13 ? 4 : 5) : (T >= 16 ? 5 : 8);
   static constexpr int kARows = T * 16;
   static constexpr int kASlot = kARows * BK;
-  static constexpr int kWSlot = kDN * BK;
+  static constexpr int kWSlot = CW * BK;
   static constexpr int kAOff = 0;
   static constexpr int kWOff = kAStages * kASlot;
   static constexpr int kSaOff = kWOff + kWStages * kWSlot;
   static constexpr int kSaInstr = (kARows + 63) / 64;
   static constexpr int kSaSlot = kSaInstr * 256;           // activation scales of one chunk
   static constexpr int kSwOff = kSaOff + kAStages * kSaSlot;
-  static constexpr int kBytes = kSwOff + kWStages * 16;
+  static constexpr int kBytes = kSwOff + kWStages * 16 + 16;   // + one word to broadcast the split state
   // Loads are split by role, because a wave's loads complete in issue order
   // (one vmcnt per wave): waves 0-3 load the activations (8 rows per
   // instruction, group g by wave g % 4) and their scales (instruction j by
-  // wave j), waves 4-7 the weight slice (16 rows each) and wave 7 the weight
-  // scale. A wave then waits only for its own stream: the activation waves
-  // for chunk c issued kAStages - 1 rounds back, the weight waves for chunk c
-  // issued kWStages - 1 rounds back, so the weight stream keeps its depth.
+  // wave j), waves 4-7 the weight slice (CW / 4 rows each) and wave 7 the
+  // weight scale. A wave then waits only for its own stream: the activation
+  // waves for chunk c issued kAStages - 1 rounds back, the weight waves for
+  // chunk c issued kWStages - 1 rounds back, so the weight stream keeps its
+  // depth.
   static constexpr int kAInstr = 2 * T;
   static constexpr int kAPerWave = (kAInstr + 3) / 4;
+  static constexpr int kWPerWave = CW / 32;
   static constexpr int ops(int w) {
-    return w < 4 ? (kAInstr / 4 + (w < kAInstr % 4 ? 1 : 0)) + (w < kSaInstr ? 1 : 0) : 2 + (w == 7 ? 1 : 0);
+    return w < 4 ? (kAInstr / 4 + (w < kAInstr % 4 ? 1 : 0)) + (w < kSaInstr ? 1 : 0)
+                 : kWPerWave + (w == 7 ? 1 : 0);
   }
   // At the start of chunk c: after its loads of chunk c a wave has issued
   // kAStages - 2 (activation waves) or kWStages - 2 (weight waves) further
@@ -102,7 +124,23 @@ struct DecodeCfg {
   static_assert(wait(0) <= 63 && wait(4) <= 63 && wait(7) <= 63, "vmcnt range");
   static_assert(kBytes <= 160 * 1024, "LDS");
   static_assert(kWStages >= kAStages, "weights are issued at least as far ahead as activations");
+  static_assert(kWStages >= 3 && kAStages >= 3, "ring depth");
 };
+
+// LDS of the largest configuration a launch can run (cmax from gemm_kernels.h).
+constexpr int kSmallBytes = cmax(DecodeCfg<1, kDN>::kBytes, DecodeCfg<2, kDN>::kBytes);
+constexpr int kNarrowBytes = cmax(cmax(cmax(DecodeCfg<3, kDN>::kBytes, DecodeCfg<4, kDN>::kBytes),
+                                       cmax(DecodeCfg<6, kDN>::kBytes, DecodeCfg<8, kDN>::kBytes)),
+                                  cmax(cmax(DecodeCfg<10, kDN>::kBytes, DecodeCfg<12, kDN>::kBytes),
+                                       cmax(DecodeCfg<14, kDN>::kBytes, DecodeCfg<16, kDN>::kBytes)));
+constexpr int kWideBytes = cmax(cmax(cmax(DecodeCfg<3, kDN2>::kBytes, DecodeCfg<4, kDN2>::kBytes),
+                                     cmax(DecodeCfg<6, kDN2>::kBytes, DecodeCfg<8, kDN2>::kBytes)),
+                                cmax(cmax(DecodeCfg<10, kDN2>::kBytes, DecodeCfg<12, kDN2>::kBytes),
+                                     cmax(DecodeCfg<14, kDN2>::kBytes, DecodeCfg<16, kDN2>::kBytes)));
+constexpr int kBigBytes = cmax(kSmallBytes, cmax(kNarrowBytes, kWideBytes));
+
+// Cache policy of the workspace's buffer accesses: sc1, device-coherent.
+constexpr int kSc1 = 16;
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -110,24 +148,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// One workgroup's work with T row subtiles (the expert's rows rounded up):
-// ring sizes, loads and MFMAs are those of DecodeCfg<T>, inside the LDS the
-// kernel allocated for its largest T.
-template <int T>
-__device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem, int e, int slice, int m0, int me) {
-  using C = DecodeCfg<T>;
+__device__ __forceinline__ uint2 bf16x4(const v4f& v) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+  uint2 packed;
+  __builtin_memcpy(&packed.x, &lo, 4);
+  __builtin_memcpy(&packed.y, &hi, 4);
+  return packed;
+}
+
+// One workgroup's work: T row subtiles (the expert's rows rounded up), CW
+// output columns from n0, K chunks [kc0, kc1); h = which K half (wide shape).
+// Ring sizes, loads and MFMAs are those of DecodeCfg<T, CW>, inside the LDS
+// the kernel allocated for its largest configuration.
+template <int T, int CW>
+__device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem, int e, int64_t n0, int kc0,
+                                             int kc1, int h, int m0, int me) {
+  using C = DecodeCfg<T, CW>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
-  const int64_t n0 = (int64_t)slice * kDN;
-  const int nc = (int)(p.k / BK);
+  const int nc = kc1 - kc0;
   const uint32_t sbase = lds_addr(smem);
 
-  const uint8_t* a_e = p.a + (int64_t)m0 * p.lda;
+  const uint8_t* a_e = p.a + (int64_t)m0 * p.lda + (int64_t)kc0 * BK;
   const uint8_t* a_end = p.a + (int64_t)(m0 + me - 1) * p.lda + p.k;
-  const uint8_t* b_e = p.b + (int64_t)e * p.n * p.ldb + n0 * p.ldb;
-  const uint8_t* b_end = b_e + (int64_t)(kDN - 1) * p.ldb + p.k;
-  const float* sb_e = p.sb + (int64_t)e * (p.n / 128) * p.ldsb + (n0 / 128) * p.ldsb;
+  const uint8_t* b_e = p.b + (int64_t)e * p.n * p.ldb + n0 * p.ldb + (int64_t)kc0 * BK;
+  const uint8_t* b_end = p.b + (int64_t)e * p.n * p.ldb + (n0 + CW - 1) * p.ldb + p.k;
+  const float* sb_e = p.sb + (int64_t)e * (p.n / 128) * p.ldsb + (n0 / 128) * p.ldsb + kc0;
+  const float* sa_e = p.sa + (int64_t)kc0 * p.ldsa + m0;
   // per-lane DMA offsets (fixed for every chunk): lane ln of an 8-row group
   // loads row 8 g + ln / 8 at the logical slot that lands in physical slot ln % 8
   const int lr = lane >> 3, ls = lane & 7;
@@ -137,11 +186,11 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
     const int row = 8 * (4 * q + (wave & 3)) + lr;
     voff_a[q] = (uint32_t)row * (uint32_t)p.lda + (uint32_t)((ls ^ swz(row)) * 16);
   }
-  uint32_t voff_w[2];                      // weight waves: rows 16 (wave - 4) + 8 h + lane / 8
+  uint32_t voff_w[C::kWPerWave];           // weight waves: rows (CW / 4) (wave - 4) + 8 i + lane / 8
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 16 * (wave & 3) + 8 * h + lr;
-    voff_w[h] = (uint32_t)row * (uint32_t)p.ldb + (uint32_t)((ls ^ swz(row)) * 16);
+  for (int i = 0; i < C::kWPerWave; ++i) {
+    const int row = (CW / 4) * (wave & 3) + 8 * i + lr;
+    voff_w[i] = (uint32_t)row * (uint32_t)p.ldb + (uint32_t)((ls ^ swz(row)) * 16);
   }
 
   // One round of loads: activations (and their scales) of chunk ca into ring
@@ -159,7 +208,7 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
       for (int q = 0; q < C::kAPerWave; ++q)
         if (4 * q + wave < C::kAInstr) dma16_buf(ra, voff_a[q], abase + (4 * q + wave) * 8 * BK);
       if (wave < C::kSaInstr) {
-        const float* s0 = p.sa + (int64_t)ca * p.ldsa + m0;
+        const float* s0 = sa_e + (int64_t)ca * p.ldsa;
         const u32x4 rs = make_rsrc(reinterpret_cast<const uint8_t*>(s0), reinterpret_cast<const uint8_t*>(s0 + me));
         dma4_buf(rs, (uint32_t)(64 * wave + lane) * 4u, sbase + C::kSaOff + as * C::kSaSlot + 64 * wave * 4);
       }
@@ -167,7 +216,8 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
       const u32x4 rw = make_rsrc(b_e + (int64_t)cw * BK, b_end);
       const uint32_t wbase = sbase + C::kWOff + ws * C::kWSlot;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma16_buf_nt(rw, voff_w[h], wbase + (16 * (wave & 3) + 8 * h) * BK);
+      for (int i = 0; i < C::kWPerWave; ++i)
+        dma16_buf_nt(rw, voff_w[i], wbase + ((CW / 4) * (wave & 3) + 8 * i) * BK);
       if (wave == 7) {
         if (lane == 0) dma4(uniform_ptr(sb_e + cw), 0u, sbase + C::kSwOff + ws * 16);
       }
@@ -183,11 +233,14 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
   const int sw = swz(l16);
   const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
   const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
-  // wave w computes row subtiles 8 q + w (q < Q) against all four weight
-  // subtiles of the slice: each activation fragment is read from LDS by one
-  // wave only (with T < 8 the waves past T only load)
-  constexpr int Q = (T + 7) / 8;
-  const bool computes = T >= 8 || wave < T;          // uniform per wave
+  // Row subtiles of this wave: 64-column shape rs(q) = 8 q + w against weight
+  // subtiles 0-3; 128-column shape rs(q) = 4 q + w / 2 against weight subtiles
+  // 4 (w % 2) .. 4 (w % 2) + 3. Subtiles at or past T are skipped (uniform
+  // per wave).
+  constexpr int kRowStep = C::kWide ? 4 : 8;
+  constexpr int Q = (T + kRowStep - 1) / kRowStep;
+  const int rs0 = C::kWide ? (wave >> 1) : wave;
+  const int cs0 = C::kWide ? 4 * (wave & 1) : 0;
   v4f acc[Q][4];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
@@ -207,100 +260,222 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
     }
     __syncthreads();
     issue(c + C::kAStages - 1, c + C::kWStages - 1);
-    if (computes) {
+    if (rs0 < T) {
       const uint8_t* as = smem + C::kAOff + (c % C::kAStages) * C::kASlot;
       const uint8_t* ws = smem + C::kWOff + (c % C::kWStages) * C::kWSlot;
       const float* sas = reinterpret_cast<const float*>(smem + C::kSaOff + (c % C::kAStages) * C::kSaSlot);
       const float swv = *reinterpret_cast<const float*>(smem + C::kSwOff + (c % C::kWStages) * 16);
       v8i wf[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = frag(ws + 16 * j * BK, off0, off1);
+      for (int j = 0; j < 4; ++j) wf[j] = frag(ws + 16 * (cs0 + j) * BK, off0, off1);
       // all MFMAs of the chunk, then their folds (no branch between them, so
       // the fragment reads and the MFMAs pipeline)
       v4f pc[Q][4];
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const v8i af = frag(as + 16 * (8 * q + wave) * BK, off0, off1);
+        if (kRowStep * q + rs0 < T) {
+          const v8i af = frag(as + 16 * (kRowStep * q + rs0) * BK, off0, off1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pc[q][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af, zero, 0, 0, 0, 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            pc[q][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af, zero, 0, 0, 0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const float sc = sas[16 * (8 * q + wave) + l16] * swv;
+        if (kRowStep * q + rs0 < T) {
+          const float sc = sas[16 * (kRowStep * q + rs0) + l16] * swv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[q][j][r] = __builtin_fmaf(pc[q][j][r], sc, acc[q][j][r]);
+            for (int r = 0; r < 4; ++r) acc[q][j][r] = __builtin_fmaf(pc[q][j][r], sc, acc[q][j][r]);
+        }
       }
     }
   }
   // the repeated loads after the last chunk must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (!computes) return;
+  if constexpr (!C::kWide) {
+    if (rs0 >= T) return;
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int r = 16 * (8 * q + wave) + l16;
-    if (r < me) {
+    for (int q = 0; q < Q; ++q) {
+      const int r = 16 * (kRowStep * q + rs0) + l16;
+      if (kRowStep * q + rs0 < T && r < me) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 lo = __builtin_convertvector((f32x2){acc[q][j][0], acc[q][j][1]}, bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2){acc[q][j][2], acc[q][j][3]}, bf16x2);
-        uint2 packed;
-        __builtin_memcpy(&packed.x, &lo, 4);
-        __builtin_memcpy(&packed.y, &hi, 4);
-        *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + n0 + 16 * j + 4 * lq) = packed;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + n0 + 16 * j + 4 * lq) = bf16x4(acc[q][j]);
       }
     }
+  } else {
+    // The two K halves of this slice meet through the workspace. Partial sums
+    // and the counter are device-coherent accesses (sc1: written through to,
+    // and read from, the level all XCDs share): a half's stores are complete
+    // (vmcnt(0)) before its counter increment, and the other half reads them
+    // only after it has seen that increment.
+    // Layout: each 16 x 16 accumulator subtile (row subtile rs, column
+    // subtile cs of the slice) is one 1 KB block, lane L's four values at
+    // 16 L bytes, so a store or load instruction moves one whole block; the
+    // slice's blocks (rs, cs) lie at (8 rs + cs) KB, t16 x 8 KB per slice, the
+    // expert's n / 128 slices in a row, the split experts one after the other,
+    // each K half's share of the workspace after the other's.
+    const int t16 = (me + 15) / 16;
+    uint32_t* cnt = p.cnt + e * kDecodeSlices + (int)(n0 / kDN2);
+    int* flag = reinterpret_cast<int*>(smem + C::kSwOff + C::kWStages * 16);
+    const int64_t col = n0 + 16 * cs0 + 4 * lq;       // + 16 j: this lane's output columns
+    auto region = [&](int half) {
+      const float* base = p.part + ((int64_t)half * p.part_subtiles + p.part_off[e]) * 16 * p.n;
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)(t16 * 16 * p.n * 4), 0x00020000);
+    };
+    const uint32_t lane_off = (uint32_t)(n0 / kDN2) * (uint32_t)t16 * 8192u + (uint32_t)lane * 16u;
+    __syncthreads();                                   // every wave is past its last LDS read
+    if (tid == 0) *flag = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    bool last = *flag == 1;                            // the other half has finished: add its sums
+    if (!last) {
+      const auto rm = region(h);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int rs = kRowStep * q + rs0;
+        if (rs < t16) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[q][j]), rm,
+                                                   lane_off + (uint32_t)(8 * rs + cs0 + j) * 1024u, 0, kSc1);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();                                 // every wave's partial sums are stored
+      if (tid == 0)
+        *flag = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      last = *flag == 1;
+    }
+    if (!last) return;                                 // uniform: the other half finishes the slice
+    const auto ro = region(1 - h);
+    v4f oth[Q][4];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int rs = kRowStep * q + rs0;
+      if (rs < t16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          oth[q][j] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_raw_buffer_load_b128(ro, lane_off + (uint32_t)(8 * rs + cs0 + j) * 1024u, 0, kSc1));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int r = 16 * (kRowStep * q + rs0) + l16;
+      if (kRowStep * q + rs0 < t16 && r < me) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + col + 16 * j) = bf16x4(acc[q][j] + oth[q][j]);
+      }
+    }
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
   }
 }
 
-template <int MT>
+// Row subtile counts with a compiled configuration: the next one at or above t16.
+template <int CW>
+__device__ __forceinline__ void dispatch_rows(const DecodeArgs& p, uint8_t* smem, int e, int64_t n0, int kc0,
+                                              int kc1, int h, int m0, int me, int t16) {
+  if constexpr (CW == kDN) {
+    if (t16 <= 1) { decode_slice<1, CW>(p, smem, e, n0, kc0, kc1, h, m0, me); return; }
+    if (t16 <= 2) { decode_slice<2, CW>(p, smem, e, n0, kc0, kc1, h, m0, me); return; }
+  }
+  if (t16 <= 3) decode_slice<3, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 4) decode_slice<4, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 6) decode_slice<6, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 8) decode_slice<8, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 10) decode_slice<10, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 12) decode_slice<12, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else if (t16 <= 14) decode_slice<14, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+  else decode_slice<16, CW>(p, smem, e, n0, kc0, kc1, h, m0, me);
+}
+
+// BIG: the launch holds an expert of more than 32 rows (all configurations,
+// the largest LDS); otherwise only the 1- and 2-subtile configurations.
+template <bool BIG>
 __global__ __launch_bounds__(512) void gemm_decode_kernel(DecodeArgs p) {
-  // DecodeCfg<T>::kBytes grows with T: the largest T sets the allocation
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeCfg<MT>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[BIG ? kBigBytes : kSmallBytes];
 
   // workgroup -> (expert, slice), expert-major: the hardware deals consecutive
   // workgroups to the 8 XCDs in turn, so each expert's slices spread over all
-  // XCDs and a large expert does not load one XCD alone
+  // XCDs and a large expert does not load one XCD alone. A split expert's
+  // workgroups 2 s and 2 s + 1 are the two K halves of its 128-column slice s.
   const int f = blockIdx.x;
-  const int e = f / p.slices, slice = f % p.slices;
+  const int e = f / p.slices, local = f % p.slices;
   const int m0 = p.row_off[e];
   const int me = p.row_off[e + 1] - m0;
-  // uniform per workgroup: an empty expert has nothing to do; otherwise the
-  // smallest T that covers its rows
+  // uniform per workgroup: an empty expert has nothing to do
   if (me <= 0) return;
-  if (me <= 16) decode_slice<1>(p, smem, e, slice, m0, me);
-  else if (me <= 32) { if constexpr (MT >= 2) decode_slice<2>(p, smem, e, slice, m0, me); }
-  else if (me <= 64) { if constexpr (MT >= 4) decode_slice<4>(p, smem, e, slice, m0, me); }
-  else if (me <= 128) { if constexpr (MT >= 8) decode_slice<8>(p, smem, e, slice, m0, me); }
-  else { if constexpr (MT >= 16) decode_slice<16>(p, smem, e, slice, m0, me); }
+  const int t16 = (me + 15) / 16;
+  const int nc = (int)(p.k / BK);
+  if (p.split[e]) {
+    if constexpr (BIG) {
+      const int h = local & 1, half = nc / 2;
+      dispatch_rows<kDN2>(p, smem, e, (int64_t)(local >> 1) * kDN2, h ? half : 0, h ? nc : half, h, m0, me, t16);
+    }
+  } else if (t16 <= 2) {
+    dispatch_rows<kDN>(p, smem, e, (int64_t)local * kDN, 0, nc, 0, m0, me, t16);
+  } else {
+    if constexpr (BIG) dispatch_rows<kDN>(p, smem, e, (int64_t)local * kDN, 0, nc, 0, m0, me, t16);
+  }
 }
 
 }  // namespace
 
+// 16-row subtiles of the experts that run split (more than 32 rows).
+static int64_t split_subtiles(int groups, const int64_t* row_off) {
+  int64_t t = 0;
+  for (int e = 0; e < groups; ++e) {
+    const int64_t rows = row_off[e + 1] - row_off[e];
+    if (rows > 32) t += (rows + 15) / 16;
+  }
+  return t;
+}
+
+int64_t grouped_gemm_decode_workspace(int groups, const int64_t* row_off, int64_t n, int64_t k) {
+  if (k / BK < 2 || n / kDN2 > kDecodeSlices) return 0;
+  const int64_t t = split_subtiles(groups, row_off);
+  if (t == 0) return 0;
+  // the counters first, at the same place for every call (kMaxGroups x
+  // kDecodeSlices words), then each K half's partial sums of the split
+  // experts' 16-row subtiles
+  return kDecodeCounterBytes + 2 * t * 16 * n * 4;
+}
+
 hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t n, int64_t k,
                                       const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                                       const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                                      uint16_t* out, int64_t ldo, hipStream_t st) {
+                                      uint16_t* out, int64_t ldo, void* workspace, hipStream_t st) {
   DecodeArgs p;
-  p.n = n; p.k = k;
+  p.n = n; p.k = k; p.m = row_off[groups];
   p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;
   p.b = b; p.ldb = ldb; p.sb = sb; p.ldsb = ldsb;
   p.out = out; p.ldo = ldo;
   p.groups = groups;
   p.slices = (int)(n / kDN);
+  const bool can_split = workspace != nullptr && k / BK >= 2 && n / kDN2 <= kDecodeSlices;
+  p.cnt = static_cast<uint32_t*>(workspace);
+  p.part = can_split ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kDecodeCounterBytes) : nullptr;
   int64_t most = 0;
   for (int e = 0; e <= groups; ++e) p.row_off[e] = (int)row_off[e];
-  for (int e = 0; e < groups; ++e) most = row_off[e + 1] - row_off[e] > most ? row_off[e + 1] - row_off[e] : most;
+  int subtiles = 0;
+  for (int e = 0; e < groups; ++e) {
+    const int64_t rows = row_off[e + 1] - row_off[e];
+    most = rows > most ? rows : most;
+    p.split[e] = (uint8_t)(can_split && rows > 32 ? 1 : 0);
+    p.part_off[e] = subtiles;
+    if (p.split[e]) subtiles += (int)((rows + 15) / 16);
+  }
+  p.part_subtiles = subtiles;
+  for (int e = groups; e < kMaxGroups; ++e) { p.split[e] = 0; p.part_off[e] = subtiles; }
   if (most == 0) return hipSuccess;
   const dim3 grid((unsigned)(groups * p.slices)), block(512);
-  if (most <= 16)       hipLaunchKernelGGL(gemm_decode_kernel<1>, grid, block, 0, st, p);
-  else if (most <= 32)  hipLaunchKernelGGL(gemm_decode_kernel<2>, grid, block, 0, st, p);
-  else if (most <= 64)  hipLaunchKernelGGL(gemm_decode_kernel<4>, grid, block, 0, st, p);
-  else if (most <= 128) hipLaunchKernelGGL(gemm_decode_kernel<8>, grid, block, 0, st, p);
-  else                  hipLaunchKernelGGL(gemm_decode_kernel<16>, grid, block, 0, st, p);
+  if (most <= 32) hipLaunchKernelGGL(gemm_decode_kernel<false>, grid, block, 0, st, p);
+  else            hipLaunchKernelGGL(gemm_decode_kernel<true>, grid, block, 0, st, p);
   return hipGetLastError();
 }
 

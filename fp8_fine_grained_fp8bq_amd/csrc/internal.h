@@ -39,6 +39,10 @@ hipError_t launch_gemm(int kind, int64_t m, int64_t n, int64_t k, const uint8_t*
 // Largest group count the grouped GEMM accepts (offsets travel as kernel arguments).
 constexpr int kMaxGroups = 256;
 constexpr int kMaxDecodeRows = 256;   // rows per group of the decode-shape grouped GEMM
+// Split decode workspace: one counter per (expert, 128-column slice) at a fixed
+// place, for up to kDecodeSlices slices (n <= 32768), then the partial sums.
+constexpr int kDecodeSlices = 256;
+constexpr int64_t kDecodeCounterBytes = (int64_t)kMaxGroups * kDecodeSlices * 4;
 
 // The same with a quantised copy of the bf16 output (FPROP / DGRAD only):
 // q [m, n] (ldq) with chunk-major 1x128 scales sq[c * ldsq + row]; out may be
@@ -52,10 +56,15 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t n, in
                                const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
                                uint16_t* out, int64_t ldo, bool pow2, hipStream_t st);
 // Grouped Fprop for decode-sized experts (each at most 256 rows, any count):
-// row_off host array of groups + 1 row offsets.
+// row_off host array of groups + 1 row offsets. workspace: null, or at least
+// grouped_gemm_decode_workspace() bytes whose counters are zero (every call
+// leaves them zero); with it, experts of more than 32 rows run as 128-column,
+// half-K workgroup pairs.
 hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t n, int64_t k,
                                       const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                                       const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
-                                      uint16_t* out, int64_t ldo, hipStream_t st);
+                                      uint16_t* out, int64_t ldo, void* workspace, hipStream_t st);
+// Bytes of workspace the split form needs (0: nothing would be split).
+int64_t grouped_gemm_decode_workspace(int groups, const int64_t* row_off, int64_t n, int64_t k);
 
 }  // namespace fp8bq

@@ -327,6 +327,43 @@ int fp8bq_grouped_gemm_decode(int32_t groups, const int64_t* row_off, int64_t n,
                               const void* b, int64_t ldb, const float* sb, int64_t ldsb,
                               void* out, int64_t ldo, int flags, void* stream);
 
+/*
+ * Bytes of workspace fp8bq_grouped_gemm_decode_ws needs for these experts and
+ * shapes: 256 KiB of counters (one per expert and 128-column slice, at the
+ * same place in every call) and 8 * m * n bytes of partial sums; 0 when no
+ * expert has more than 32 rows, k < 256 or n > 32768 (nothing is split then). Arguments as fp8bq_grouped_gemm_decode; *bytes receives the size.
+ * Errors: E_INVAL (null bytes or row_off, groups out of range), E_SHAPE (bad
+ * offsets, as fp8bq_grouped_gemm_decode).
+ */
+int fp8bq_grouped_gemm_decode_workspace_size(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                                             int64_t* bytes);
+
+/*
+ * fp8bq_grouped_gemm_decode with a workspace. Experts of more than 32 rows
+ * then run as pairs of workgroups over the two halves of K, each for 128
+ * output columns (half the activation bytes per output column of the
+ * 64-column, full-K workgroups, which bound the larger experts): each half
+ * stores its FP32 partial sums in the workspace and the second to finish adds
+ * the other's and writes the bf16 output. The result is deterministic (a sum
+ * of two terms does not depend on their order) and differs from
+ * fp8bq_grouped_gemm_decode's only in the order the FP32 chunk sums are added.
+ *
+ * workspace        device memory of at least workspace_bytes >= the size
+ *                  fp8bq_grouped_gemm_decode_workspace_size gives (NULL allowed
+ *                  when that size is 0), 16-byte aligned, owned by the caller.
+ *                  It must be zero-filled before its first use; every call
+ *                  leaves its counters zero again, so a workspace is reused
+ *                  without clearing. Calls that share a workspace must not run
+ *                  concurrently (they would share counters).
+ * Other arguments and errors as fp8bq_grouped_gemm_decode; E_INVAL for a
+ * missing or too small workspace, E_ALIGN for a misaligned one.
+ */
+int fp8bq_grouped_gemm_decode_ws(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                                 const void* a, int64_t lda, const float* sa, int64_t ldsa,
+                                 const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                                 void* out, int64_t ldo, void* workspace, int64_t workspace_bytes,
+                                 int flags, void* stream);
+
 /* Thread-local description of the last non-OK status on this thread. */
 const char* fp8bq_last_error(void);
 

@@ -89,11 +89,20 @@ hipError_t launch_grouped_gemm(int groups, const int64_t* row_off, int64_t, int6
     if (row_off[e + 1] < row_off[e] || row_off[e] % 128) std::abort();
   return LAUNCHED();
 }
-hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t, int64_t, const uint8_t*,
+int64_t grouped_gemm_decode_workspace(int groups, const int64_t* row_off, int64_t n, int64_t k) {
+  // the library's rule: counters, then both K halves' partial sums of the split experts' 16-row subtiles
+  int64_t t = 0;
+  for (int e = 0; e < groups; ++e)
+    if (row_off[e + 1] - row_off[e] > 32) t += (row_off[e + 1] - row_off[e] + 15) / 16;
+  if (t == 0 || k / 128 < 2 || n / 128 > 256) return 0;
+  return 256 * 256 * 4 + 2 * t * 16 * n * 4;
+}
+hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t n, int64_t k, const uint8_t*,
                                       int64_t, const float*, int64_t, const uint8_t*, int64_t, const float*,
-                                      int64_t, uint16_t*, int64_t, hipStream_t) {
+                                      int64_t, uint16_t*, int64_t, void* workspace, hipStream_t) {
   for (int e = 0; e < groups; ++e)
     if (row_off[e + 1] < row_off[e] || row_off[e + 1] - row_off[e] > 256) std::abort();
+  if (workspace && grouped_gemm_decode_workspace(groups, row_off, n, k) == 0) std::abort();
   return LAUNCHED();
 }
 }  // namespace fp8bq
@@ -227,6 +236,27 @@ static void validation() {
   EXPECT(fp8bq_grouped_gemm_decode(2, doff_big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_SHAPE);
   EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, 2000, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2000, 0, nullptr), FP8BQ_E_SHAPE);
   EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, 2048, 7168, P(A16 + 8), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16), 2048, 0, nullptr), FP8BQ_E_ALIGN);
+  // the workspace form: size query, missing / small / misaligned workspace
+  {
+    const int64_t big[3] = {0, 217, 260};                  // one expert above 32 rows: split
+    int64_t need = -1;
+    EXPECT(fp8bq_grouped_gemm_decode_workspace_size(2, big, 2048, 7168, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_grouped_gemm_decode_workspace_size(2, doff_big, 2048, 7168, &need), FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_grouped_gemm_decode_workspace_size(2, big, 2000, 7168, &need), FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_grouped_gemm_decode_workspace_size(2, big, 2048, 7168, &need), FP8BQ_OK);
+    if (need != 262144 + 2 * 17 * 16 * 2048 * 4) { std::printf("workspace size %lld\n", (long long)need); ++g_fail; }
+    EXPECT(fp8bq_grouped_gemm_decode_workspace_size(2, doff_ok, 2048, 7168, &need), FP8BQ_OK);
+    if (need != 0) { std::printf("workspace size %lld for small experts\n", (long long)need); ++g_fail; }
+    const int64_t w = 262144 + 2 * 17 * 16 * 2048 * 4;
+    EXPECT(fp8bq_grouped_gemm_decode_ws(2, big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16),
+                                        2048, nullptr, w, 0, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_grouped_gemm_decode_ws(2, big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16),
+                                        2048, P(Q16), w - 1, 0, nullptr), FP8BQ_E_INVAL);
+    EXPECT(fp8bq_grouped_gemm_decode_ws(2, big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16),
+                                        2048, P(Q16 + 8), w, 0, nullptr), FP8BQ_E_ALIGN);
+    EXPECT(fp8bq_grouped_gemm_decode_ws(2, big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16),
+                                        2048, P(Q16), w, 1, nullptr), FP8BQ_E_INVAL);
+  }
   // sizes whose products do not fit in 64 bits
   const int64_t huge = INT64_MAX - 127;
   EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, huge / 128 * 128, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168,
@@ -266,8 +296,16 @@ static void accepted(int want) {
                             0, nullptr), want);
   int64_t doff[257];
   for (int e = 0; e <= 256; ++e) doff[e] = 7 * (int64_t)e;
+  const int64_t doff_ok_small[3] = {0, 30, 50};
   EXPECT(fp8bq_grouped_gemm_decode(256, doff, 2048, 7168, P(A16), 7168, F(S4), 1792, P(B16), 7168, F(S4), 56,
                                    P(O16), 2048, 0, nullptr), want);
+  int64_t doff2[257];
+  for (int e = 0; e <= 256; ++e) doff2[e] = 256 * (int64_t)e;      // 256 experts of 256 rows: all split
+  const int64_t w2 = 262144 + 2 * 4096 * 16 * (int64_t)2048 * 4;
+  EXPECT(fp8bq_grouped_gemm_decode_ws(256, doff2, 2048, 7168, P(A16), 7168, F(S4), 65536, P(B16), 7168, F(S4), 56,
+                                      P(O16), 2048, P(Q16), w2, 0, nullptr), want);
+  EXPECT(fp8bq_grouped_gemm_decode_ws(2, doff_ok_small, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56,
+                                      P(O16), 2048, nullptr, 0, 0, nullptr), want);       // nothing split: no workspace
 }
 
 int main() {
