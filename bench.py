@@ -164,7 +164,9 @@ def status_table(path):
         g = v["decode_grouped"]
         rows.append(("NEXT-4 decode grouped Fprop (853 rows, 8 × [2048, 7168])", g["kernel"],
                      f"{g['us']:.1f} µs cold ({spread(g.get('us_stats'))}), {g['GBps'] / 1000:.2f} TB/s = "
-                     f"{pct(g['roofline']['frac'])} of 8 TB/s"))
+                     f"{pct(g['roofline']['frac'])} of 8 TB/s"
+                     + (f"; without workspace (64-column full-K workgroups) {g['full_k_us']:.1f} µs"
+                        if "full_k_us" in g else "")))
     c = d.get("cpu_baseline")
     if c:
         rows.append(("CPU oracle (numpy)", "oracle/", f"{c['value'] * 1000:.1f} GFLOP/s on {c['cores']} host threads ({c['sample']})"))
@@ -175,7 +177,8 @@ def status_table(path):
 
 
 # kernels that --leg launches alone (each on the workload the bench times it on)
-LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "mfma_stream",
+LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "decode_fullk",
+        "mfma_stream",
         "cache_e5m6", "uncache_e5m6", "requant_e5m6")
 
 
@@ -195,7 +198,8 @@ def run_leg(args):
     torch.cuda.set_device(0)
     sp = torch.cuda.current_stream(dev).cuda_stream
     leg = args.leg
-    cold = leg in ("quant_x", "quant_w", "qcol", "decode", "cache_e5m6", "uncache_e5m6", "requant_e5m6")
+    cold = leg in ("quant_x", "quant_w", "qcol", "decode", "decode_fullk", "cache_e5m6", "uncache_e5m6",
+                   "requant_e5m6")
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
     flops = nbytes = None
 
@@ -304,7 +308,7 @@ def run_leg(args):
                 def fn():
                     fb.fp8bq_gemm(fb.WGRAD, Nd, Kd, Md, o_dqt.data_ptr(), Md, o_dst.data_ptr(), Nd, o_xqt.data_ptr(),
                                   Md, o_xst.data_ptr(), Kd, o_dw.data_ptr(), Kd, sp)
-    elif leg == "decode":
+    elif leg in ("decode", "decode_fullk"):
         dec = workloads.moe_decode()
         G_d, N_d, K_d = dec.w.shape
         m_d = int(dec.row_off[-1])
@@ -320,9 +324,18 @@ def run_leg(args):
         nbytes = (G_d * N_d * K_d + G_d * (N_d // 128) * (K_d // 128) * 4 + m_d * K_d + m_d * (K_d // 128) * 4
                   + m_d * N_d * 2)
 
+        d_need = fb.fp8bq_grouped_gemm_decode_workspace_size(G_d, d_off, N_d, K_d)
+        d_wsp = fb.decode_workspace(d_need, dev)
+
         def fn():
-            fb.fp8bq_grouped_gemm_decode(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
-                                         d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d, 0, sp)
+            if leg == "decode":
+                fb.fp8bq_grouped_gemm_decode_ws(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
+                                                d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(),
+                                                N_d, d_wsp.data_ptr(), d_wsp.numel(), 0, sp)
+            else:
+                fb.fp8bq_grouped_gemm_decode(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
+                                             d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d,
+                                             0, sp)
     else:   # mfma_stream: the matrix-unit probe without promotion (reference for the busy counters)
         from fp8_fine_grained_fp8bq_amd import probe
         codes = torch.randint(0, 0x7F, (1 << 22,), dtype=torch.uint8, device=dev)
@@ -685,10 +698,22 @@ def main():
     d_y = torch.empty((m_d, N_d), dtype=torch.bfloat16, device=dev)
     d_off = [int(v) for v in dec.row_off]
 
+    # the workspace form (experts above 32 rows as 128-column half-K pairs); its
+    # workspace is allocated and zeroed here, outside the timed region
+    d_need = fb.fp8bq_grouped_gemm_decode_workspace_size(G_d, d_off, N_d, K_d)
+    d_wsp = fb.decode_workspace(d_need, dev)
+
     def decode():
+        fb.fp8bq_grouped_gemm_decode_ws(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
+                                        d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d,
+                                        d_wsp.data_ptr(), d_wsp.numel(), 0, sp)
+
+    def decode_fullk():
         fb.fp8bq_grouped_gemm_decode(G_d, d_off, N_d, K_d, d_xq.data_ptr(), K_d, d_xs.data_ptr(), m_d,
                                      d_wq.data_ptr(), K_d, d_ws.data_ptr(), K_d // 128, d_y.data_ptr(), N_d, 0, sp)
 
+    decode_fullk()
+    st_t_dec0 = time_kernel(decode_fullk, args.kernel_reps, True)
     decode()
     st_t_dec = time_kernel(decode, args.kernel_reps, True)
     t_dec = st_t_dec["mean"]
@@ -1046,7 +1071,10 @@ def main():
                              "traffic": None},
                 "algorithmic_bytes": bytes_dec,
                 "TFLOPs": round(2.0 * m_d * N_d * K_d / (t_dec * 1e-6) / 1e12, 1),
-                "kernel": "gemm_decode_kernel",
+                "kernel": "gemm_decode_kernel<true> (fp8bq_grouped_gemm_decode_ws)",
+                "workspace_bytes": d_need,
+                "full_k_us": round(st_t_dec0["mean"], 2), "full_k_us_stats": rnd(st_t_dec0),
+                "full_k_kernel": "gemm_decode_kernel<true> (fp8bq_grouped_gemm_decode, no workspace)",
             },
         },
     }
