@@ -11,7 +11,7 @@ Two layers with the C names:
 * `fp8bq_quant_act_1x128`, `fp8bq_quant_w_128x128`, `fp8bq_requant_t_128x1`,
   `fp8bq_gemm`, `fp8bq_gemm_quant`, `fp8bq_grouped_gemm`,
   `fp8bq_grouped_gemm_decode`, `fp8bq_grouped_gemm_decode_workspace_size`,
-  `fp8bq_grouped_gemm_decode_ws`, `fp8bq_cache_e5m6_1x128`,
+  `fp8bq_grouped_gemm_decode_ws`, `fp8bq_grouped_gemm_decode_noalloc`, `fp8bq_cache_e5m6_1x128`,
   `fp8bq_uncache_e5m6_1x128`, `fp8bq_requant_e5m6_t_128x1`: pointer-level, exactly the C signatures (ints
   for pointers and the stream); a non-zero status raises `Fp8bqError`.
 * `quant_act_1x128`, `quant_w_128x128`, `requant_t_128x1`, `gemm`,
@@ -37,7 +37,8 @@ SCALE_POW2 = 0x10   # power-of-two scales (OR into the act mode / gemm op; `flag
 
 EXPORTS = ("fp8bq_quant_act_1x128", "fp8bq_quant_w_128x128", "fp8bq_requant_t_128x1", "fp8bq_gemm",
            "fp8bq_gemm_quant", "fp8bq_grouped_gemm", "fp8bq_grouped_gemm_decode",
-           "fp8bq_grouped_gemm_decode_workspace_size", "fp8bq_grouped_gemm_decode_ws", "fp8bq_cache_e5m6_1x128",
+           "fp8bq_grouped_gemm_decode_workspace_size", "fp8bq_grouped_gemm_decode_ws",
+           "fp8bq_grouped_gemm_decode_noalloc", "fp8bq_cache_e5m6_1x128",
            "fp8bq_uncache_e5m6_1x128", "fp8bq_requant_e5m6_t_128x1", "fp8bq_last_error", "fp8bq_version")
 
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_grouped_gemm_decode_ws.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), i64, i64,
                                                    vp, i64, fp, i64, vp, i64, fp, i64, vp, i64, vp, i64, i32, vp]
         L.fp8bq_grouped_gemm_decode_ws.restype = ctypes.c_int
+        L.fp8bq_grouped_gemm_decode_noalloc.argtypes = L.fp8bq_grouped_gemm.argtypes
+        L.fp8bq_grouped_gemm_decode_noalloc.restype = ctypes.c_int
         L.fp8bq_last_error.argtypes = []
         L.fp8bq_version.restype = ctypes.c_char_p
         L.fp8bq_version.argtypes = []
@@ -340,6 +343,15 @@ def fp8bq_grouped_gemm_decode_ws(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb
                                                      ldb, sb, ldsb, out, ldo, workspace, workspace_bytes, flags,
                                                      stream))
 
+
+def fp8bq_grouped_gemm_decode_noalloc(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo, flags=0,
+                                      stream=0):
+    return _check("fp8bq_grouped_gemm_decode_noalloc",
+                  lib().fp8bq_grouped_gemm_decode_noalloc(groups, _offsets(groups, row_off), n, k, a, lda, sa, ldsa, b,
+                                                          ldb, sb, ldsb, out, ldo, flags, stream))
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _workspaces = {}
 

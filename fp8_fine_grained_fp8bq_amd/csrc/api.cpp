@@ -12,6 +12,8 @@
 
 #include "internal.h"
 
+static_assert(FP8BQ_DECODE_NOALLOC_SCRATCH_BYTES == fp8bq::kNoAllocScratchBytes, "scratch size in the header");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -376,6 +378,32 @@ int fp8bq_grouped_gemm_decode_ws(int32_t groups, const int64_t* row_off, int64_t
                                                     static_cast<uint16_t*>(out), ldo, need > 0 ? workspace : nullptr,
                                                     reinterpret_cast<hipStream_t>(stream)),
                   "grouped_gemm_decode_ws");
+}
+
+int fp8bq_grouped_gemm_decode_noalloc(int32_t groups, const int64_t* row_off, int64_t n, int64_t k, const void* a,
+                                      int64_t lda, const float* sa, int64_t ldsa, const void* b, int64_t ldb,
+                                      const float* sb, int64_t ldsb, void* out, int64_t ldo, int flags,
+                                      void* stream) {
+  if (int st = check_decode("grouped_gemm_decode_noalloc", groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb,
+                            out, ldo, flags))
+    return st;
+  const int64_t need = fp8bq::grouped_gemm_decode_workspace(groups, row_off, n, k);
+  if (need > fp8bq::kNoAllocScratchBytes)
+    return fail(FP8BQ_E_SHAPE,
+                "grouped_gemm_decode_noalloc: these experts need %lld bytes of scratch, the library holds %lld per "
+                "device (pass a workspace to fp8bq_grouped_gemm_decode_ws instead)",
+                (long long)need, (long long)fp8bq::kNoAllocScratchBytes);
+  if (int st = check_device()) return st;
+  if (row_off[groups] == 0) return FP8BQ_OK;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  return launched(need > 0
+                      ? fp8bq::launch_grouped_gemm_decode_noalloc(groups, row_off, n, k, static_cast<const uint8_t*>(a),
+                                                                  lda, sa, ldsa, static_cast<const uint8_t*>(b), ldb,
+                                                                  sb, ldsb, static_cast<uint16_t*>(out), ldo, hs)
+                      : fp8bq::launch_grouped_gemm_decode(groups, row_off, n, k, static_cast<const uint8_t*>(a), lda,
+                                                          sa, ldsa, static_cast<const uint8_t*>(b), ldb, sb, ldsb,
+                                                          static_cast<uint16_t*>(out), ldo, nullptr, hs),
+                  "grouped_gemm_decode_noalloc");
 }
 
 }  // extern "C"

@@ -50,6 +50,19 @@
 //    against 53.9 us for one 217-row expert among 1-row ones.
 #include "gemm_kernels.h"
 
+#include <mutex>
+
+// Scratch of fp8bq_grouped_gemm_decode_noalloc, the split form for callers
+// that cannot allocate: its workspace (the counters, then the partial sums)
+// lives here, kNoAllocScratchBytes per device, held until the process ends.
+// Every call on a device shares that device's copy. The counters start at zero
+// (the array is zero when the code object is loaded on a device) and every
+// call leaves them at zero; the partial sums need no clearing (a K half reads
+// only what its partner stored in the same call). Calls that overlap on one
+// device race. Host code never passes this name to a kernel: it is a host-side
+// stand-in; the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[fp8bq::kNoAllocScratchBytes];
+
 namespace fp8bq {
 namespace {
 
@@ -479,6 +492,33 @@ hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_
   if (most <= 32) hipLaunchKernelGGL(gemm_decode_kernel<false>, grid, block, 0, st, p);
   else            hipLaunchKernelGGL(gemm_decode_kernel<true>, grid, block, 0, st, p);
   return hipGetLastError();
+}
+
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+}  // namespace
+
+hipError_t launch_grouped_gemm_decode_noalloc(int groups, const int64_t* row_off, int64_t n, int64_t k,
+                                              const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                              const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
+                                              uint16_t* out, int64_t ldo, hipStream_t st) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current: the address of its copy
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  return launch_grouped_gemm_decode(groups, row_off, n, k, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, ldo,
+                                    g_scratch_ptr[dev], st);
 }
 
 }  // namespace fp8bq

@@ -66,5 +66,13 @@ hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_
                                       uint16_t* out, int64_t ldo, void* workspace, hipStream_t st);
 // Bytes of workspace the split form needs (0: nothing would be split).
 int64_t grouped_gemm_decode_workspace(int groups, const int64_t* row_off, int64_t n, int64_t k);
+// The split form with the library's own scratch (kNoAllocScratchBytes per
+// device, a static device array) as its workspace: allocates nothing. The
+// caller has checked that the workspace it needs fits.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)32 << 20;
+hipError_t launch_grouped_gemm_decode_noalloc(int groups, const int64_t* row_off, int64_t n, int64_t k,
+                                              const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                              const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
+                                              uint16_t* out, int64_t ldo, hipStream_t st);
 
 }  // namespace fp8bq

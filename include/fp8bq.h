@@ -364,6 +364,27 @@ int fp8bq_grouped_gemm_decode_ws(int32_t groups, const int64_t* row_off, int64_t
                                  void* out, int64_t ldo, void* workspace, int64_t workspace_bytes,
                                  int flags, void* stream);
 
+/*
+ * fp8bq_grouped_gemm_decode_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the workspace is the library's own scratch, a static device
+ * array of 32 MiB (FP8BQ_DECODE_NOALLOC_SCRATCH_BYTES) on each device the
+ * library runs on, held until the process ends. The call allocates nothing.
+ * Results are bit for bit those of fp8bq_grouped_gemm_decode_ws.
+ *
+ * Every call on a device shares that device's scratch: calls that overlap on
+ * one device (e.g. on two streams) race. The scratch's counters start at zero
+ * and every call leaves them at zero.
+ * Arguments as fp8bq_grouped_gemm_decode. Errors as fp8bq_grouped_gemm_decode;
+ * E_SHAPE when the workspace these experts need
+ * (fp8bq_grouped_gemm_decode_workspace_size) exceeds the scratch.
+ */
+enum { FP8BQ_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+int fp8bq_grouped_gemm_decode_noalloc(int32_t groups, const int64_t* row_off, int64_t n, int64_t k,
+                                      const void* a, int64_t lda, const float* sa, int64_t ldsa,
+                                      const void* b, int64_t ldb, const float* sb, int64_t ldsb,
+                                      void* out, int64_t ldo, int flags, void* stream);
+
 /* Thread-local description of the last non-OK status on this thread. */
 const char* fp8bq_last_error(void);
 

@@ -97,6 +97,13 @@ int64_t grouped_gemm_decode_workspace(int groups, const int64_t* row_off, int64_
   if (t == 0 || k / 128 < 2 || n / 128 > 256) return 0;
   return 256 * 256 * 4 + 2 * t * 16 * n * 4;
 }
+hipError_t launch_grouped_gemm_decode_noalloc(int groups, const int64_t* row_off, int64_t n, int64_t k,
+                                              const uint8_t*, int64_t, const float*, int64_t, const uint8_t*,
+                                              int64_t, const float*, int64_t, uint16_t*, int64_t, hipStream_t) {
+  const int64_t need = grouped_gemm_decode_workspace(groups, row_off, n, k);
+  if (need <= 0 || need > ((int64_t)32 << 20)) std::abort();   // the scratch: 32 MiB
+  return LAUNCHED();
+}
 hipError_t launch_grouped_gemm_decode(int groups, const int64_t* row_off, int64_t n, int64_t k, const uint8_t*,
                                       int64_t, const float*, int64_t, const uint8_t*, int64_t, const float*,
                                       int64_t, uint16_t*, int64_t, void* workspace, hipStream_t) {
@@ -257,6 +264,15 @@ static void validation() {
     EXPECT(fp8bq_grouped_gemm_decode_ws(2, big, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56, P(O16),
                                         2048, P(Q16), w, 1, nullptr), FP8BQ_E_INVAL);
   }
+  // the allocation-free form: a launch whose workspace exceeds the scratch is refused
+  {
+    int64_t big8[9];
+    for (int e = 0; e <= 8; ++e) big8[e] = 256 * (int64_t)e;     // 8 x 256 rows at n = 4096: 64 MiB of partial sums
+    EXPECT(fp8bq_grouped_gemm_decode_noalloc(8, big8, 4096, 7168, P(A16), 7168, F(S4), 2048, P(B16), 7168, F(S4), 56,
+                                             P(O16), 4096, 0, nullptr), FP8BQ_E_SHAPE);
+    EXPECT(fp8bq_grouped_gemm_decode_noalloc(8, big8, 4096, 7168, P(A16), 7168, F(S4), 2048, P(B16), 7168, F(S4), 56,
+                                             P(O16), 4096, 1, nullptr), FP8BQ_E_INVAL);
+  }
   // sizes whose products do not fit in 64 bits
   const int64_t huge = INT64_MAX - 127;
   EXPECT(fp8bq_grouped_gemm_decode(2, doff_ok, huge / 128 * 128, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168,
@@ -306,6 +322,11 @@ static void accepted(int want) {
                                       P(O16), 2048, P(Q16), w2, 0, nullptr), want);
   EXPECT(fp8bq_grouped_gemm_decode_ws(2, doff_ok_small, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168, F(S4), 56,
                                       P(O16), 2048, nullptr, 0, 0, nullptr), want);       // nothing split: no workspace
+  const int64_t dmix[9] = {0, 217, 396, 516, 609, 684, 741, 810, 853};     // the 256-token decode step: fits
+  EXPECT(fp8bq_grouped_gemm_decode_noalloc(8, dmix, 2048, 7168, P(A16), 7168, F(S4), 853, P(B16), 7168, F(S4), 56,
+                                           P(O16), 2048, 0, nullptr), want);
+  EXPECT(fp8bq_grouped_gemm_decode_noalloc(2, doff_ok_small, 2048, 7168, P(A16), 7168, F(S4), 512, P(B16), 7168,
+                                           F(S4), 56, P(O16), 2048, 0, nullptr), want);
 }
 
 int main() {
