@@ -275,6 +275,36 @@ def test_grouped_decode_validation(L):
     assert _st(L, f, 2, off(0, 30, 50), *bad[1:]) == fb.E_ALIGN
 
 
+def test_grouped_decode_workspace_forms_validation(L):
+    def off(*v):
+        return (ctypes.c_int64 * len(v))(*v)
+    big = off(0, 217, 260)                       # 217 and 43 rows: both split (14 + 3 subtiles of 16 rows)
+    need = ctypes.c_int64(-1)
+    assert L.fp8bq_grouped_gemm_decode_workspace_size(2, big, 2048, 7168, ctypes.byref(need)) == fb.OK
+    assert need.value == 256 * 256 * 4 + 2 * 17 * 16 * 2048 * 4
+    assert fb.fp8bq_grouped_gemm_decode_workspace_size(2, [0, 30, 50], 2048, 7168) == 0    # nothing split
+    assert fb.fp8bq_grouped_gemm_decode_workspace_size(2, [0, 217, 260], 2048, 128) == 0   # one chunk: no halves
+    assert fb.fp8bq_grouped_gemm_decode_workspace_size(2, [0, 217, 260], 128 * 257, 7168) == 0   # n > 32768
+    assert L.fp8bq_grouped_gemm_decode_workspace_size(2, big, 2048, 7168, None) == fb.E_INVAL
+    assert L.fp8bq_grouped_gemm_decode_workspace_size(2, off(0, 300, 310), 2048, 7168, ctypes.byref(need)) == fb.E_SHAPE
+    f = "fp8bq_grouped_gemm_decode_ws"
+    args = [2048, 7168, A16, 7168, S4, 512, B16, 7168, S4, 56, O16, 2048]
+    w = need.value
+    assert _st(L, f, 2, big, *args, Q16, w, 0, None) == fb.E_DEVICE
+    assert _st(L, f, 2, big, *args, None, w, 0, None) == fb.E_INVAL                     # workspace missing
+    assert "workspace" in L.fp8bq_last_error().decode()
+    assert _st(L, f, 2, big, *args, Q16, w - 1, 0, None) == fb.E_INVAL                  # too small
+    assert _st(L, f, 2, big, *args, Q16 + 8, w, 0, None) == fb.E_ALIGN
+    assert _st(L, f, 2, big, *args, Q16, w, 1, None) == fb.E_INVAL                      # flags
+    assert _st(L, f, 2, off(0, 30, 50), *args, None, 0, 0, None) == fb.E_DEVICE         # no workspace needed
+    f = "fp8bq_grouped_gemm_decode_noalloc"
+    assert _st(L, f, 2, big, *args, 0, None) == fb.E_DEVICE
+    assert _st(L, f, 2, big, *args, 1, None) == fb.E_INVAL
+    huge = off(*[256 * e for e in range(9)])     # 8 x 256 rows at n = 4096: 64 MiB of partial sums
+    assert _st(L, f, 8, huge, 4096, 7168, A16, 7168, S4, 2048, B16, 7168, S4, 56, O16, 4096, 0, None) == fb.E_SHAPE
+    assert "scratch" in L.fp8bq_last_error().decode()
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(fb.Fp8bqError) as ei:
         fb.fp8bq_gemm(7, 1, 128, 128, A16, 128, S4, 1, B16, 128, S4, 1, O16, 128, 0)
