@@ -22,25 +22,29 @@
 //    stores its partial sums with device-coherent stores and bumps a counter;
 //    the second to finish adds the other's partial (two-term sums are the
 //    same in either order) and writes the bf16 output. Nobody waits.
-//  * 8 waves (more waves issue the loads: each load instruction keeps its
-//    wave for a while). The expert's rows are T subtiles of 16, T the next
-//    available count at or above rows / 16 (1, 2, 3, 4, 6, 8, 10, 12, 14 or 16;
-//    rows past the expert's end read as zeros through the buffer bound and are
-//    never stored). 64-column shape: wave w computes row subtiles w, w + 8
-//    against the slice's four weight subtiles. 128-column shape: wave w
-//    computes the four weight subtiles of column half w % 2 against row
-//    subtiles w / 2, w / 2 + 4, ... Either way a 64 or 128 column slice lies
-//    inside one 128 x 128 weight block: a chunk has one weight scale.
+//  * 8 waves with fixed roles: waves 0-3 compute, waves 4-5 stream the weight
+//    slice, waves 6-7 the expert's rows. The expert's rows are T subtiles of
+//    16, T the next available count at or above rows / 16 (1, 2, 3, 4, 6, 8,
+//    10, 12, 14 or 16; rows past the expert's end read as zeros through the
+//    buffer bound and are never stored). 64-column shape: compute wave w takes
+//    the slice's four weight subtiles against row subtiles w, w + 4, ...;
+//    128-column shape: the four weight subtiles of column half w % 2 against
+//    row subtiles w / 2, w / 2 + 2, ... Either way a 64 or 128 column slice
+//    lies inside one 128 x 128 weight block: a chunk has one weight scale.
+//    With every wave both loading and computing, a wave stalled on a full
+//    memory queue could not compute and the memory pipeline idled while the
+//    waves computed: the 256-token decode mix took 51.2 us, 42.8 us with the
+//    roles separated.
 //  * The weight slice streams through an LDS ring of kWStages chunks with
 //    global -> LDS DMA (non-temporal: each weight byte is read once), issued
 //    kWStages - 1 chunks ahead; the activation rows (mostly L2 hits: every
 //    column slice of the expert reads them) through a ring of kAStages chunks.
-//  * One barrier per chunk; before it each wave waits only until its own DMA
+//  * One barrier per chunk; before it each loader waits only until its own DMA
 //    for the chunk has landed (vmcnt counted from the fixed issue pattern, with
-//    the final chunks re-issued so that the count stays exact). The loads are
-//    split between waves by operand (activation waves, weight waves): a wave's
-//    loads complete in issue order, so a wave that waited for the activations
-//    of chunk c would also wait for every older weight load.
+//    the final chunks re-issued so that the count stays exact). Each loader
+//    carries one stream: a wave's loads complete in issue order, so a wave
+//    that waited for the activations of chunk c would also wait for every
+//    older weight load.
 //  * Workgroups are expert-major in launch order, which the hardware deals
 //    to the 8 XCDs in turn: each expert's column slices spread over all XCDs.
 //    With skewed expert sizes this beats keeping an expert's slices on one
@@ -116,27 +120,26 @@ struct DecodeCfg {
   static constexpr int kSaSlot = kSaInstr * 256;           // activation scales of one chunk
   static constexpr int kSwOff = kSaOff + kAStages * kSaSlot;
   static constexpr int kBytes = kSwOff + kWStages * 16 + 16;   // + one word to broadcast the split state
-  // Loads are split by role, because a wave's loads complete in issue order
-  // (one vmcnt per wave): waves 0-3 load the activations (8 rows per
-  // instruction, group g by wave g % 4) and their scales (instruction j by
-  // wave j), waves 4-7 the weight slice (CW / 4 rows each) and wave 7 the
-  // weight scale. A wave then waits only for its own stream: the activation
-  // waves for chunk c issued kAStages - 1 rounds back, the weight waves for
-  // chunk c issued kWStages - 1 rounds back, so the weight stream keeps its
-  // depth.
+  // Waves 0-3 only compute; waves 4-7 only load, one stream per wave, because a
+  // wave's loads complete in issue order (one vmcnt per wave): waves 4 and 5 the
+  // weight slice (8-row instruction i by wave 4 + i % 2) and wave 5 its scale,
+  // waves 6 and 7 the activation rows (instruction i by wave 6 + i % 2) and
+  // their scales (instruction j by wave 6 + j % 2). A loader stalled on a full
+  // memory queue delays no arithmetic, and the compute waves hold no loads, so
+  // nothing makes them wait on memory but the barrier (with every wave both
+  // loading and computing, switching the arithmetic off made the kernel
+  // 18-20% faster: the two were serialised).
   static constexpr int kAInstr = 2 * T;
-  static constexpr int kAPerWave = (kAInstr + 3) / 4;
-  static constexpr int kWPerWave = CW / 32;
-  static constexpr int ops(int w) {
-    return w < 4 ? (kAInstr / 4 + (w < kAInstr % 4 ? 1 : 0)) + (w < kSaInstr ? 1 : 0)
-                 : kWPerWave + (w == 7 ? 1 : 0);
+  static constexpr int kWInstr = CW / 8;
+  static constexpr int ops(int w) {   // loads per round of loader wave w
+    return w < 6 ? kWInstr / 2 + (w == 5 ? 1 : 0) : kAInstr / 2 + kSaInstr / 2 + (w == 6 ? kSaInstr % 2 : 0);
   }
   // At the start of chunk c: after its loads of chunk c a wave has issued
   // kAStages - 2 (activation waves) or kWStages - 2 (weight waves) further
   // rounds; waiting until at most that many loads are outstanding leaves
   // chunk c's loads landed.
-  static constexpr int wait(int w) { return (w < 4 ? kAStages - 2 : kWStages - 2) * ops(w); }
-  static_assert(wait(0) <= 63 && wait(4) <= 63 && wait(7) <= 63, "vmcnt range");
+  static constexpr int wait(int w) { return (w < 6 ? kWStages - 2 : kAStages - 2) * ops(w); }
+  static_assert((kWStages - 1) * ops(5) <= 63 && (kAStages - 1) * ops(6) <= 63, "vmcnt range");
   static_assert(kBytes <= 160 * 1024, "LDS");
   static_assert(kWStages >= kAStages, "weights are issued at least as far ahead as activations");
   static_assert(kWStages >= 3 && kAStages >= 3, "ring depth");
@@ -192,20 +195,19 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
   const uint8_t* b_end = p.b + (int64_t)e * p.n * p.ldb + (n0 + CW - 1) * p.ldb + p.k;
   const float* sb_e = p.sb + (int64_t)e * (p.n / 128) * p.ldsb + (n0 / 128) * p.ldsb + kc0;
   const float* sa_e = p.sa + (int64_t)kc0 * p.ldsa + m0;
-  // per-lane DMA offsets (fixed for every chunk): lane ln of an 8-row group
-  // loads row 8 g + ln / 8 at the logical slot that lands in physical slot ln % 8
-  const int lr = lane >> 3, ls = lane & 7;
-  uint32_t voff_a[C::kAPerWave];          // activation waves: groups 4 q + wave
+  // per-lane DMA offsets of a loader wave (fixed for every chunk): lane ln of an
+  // 8-row group loads row 8 g + ln / 8 at the logical slot that lands in
+  // physical slot ln % 8; instruction i of wave 4 + h (weights) or 6 + h
+  // (activations) is group g = 2 i + h
+  const int lr = lane >> 3, ls = lane & 7, h2 = wave & 1;
+  const bool wload = wave == 4 || wave == 5, aload = wave >= 6;
+  constexpr int kAPer = C::kAInstr / 2, kWPer = C::kWInstr / 2;
+  constexpr int kPer = kAPer > kWPer ? kAPer : kWPer;
+  uint32_t voff[kPer];
 #pragma unroll
-  for (int q = 0; q < C::kAPerWave; ++q) {
-    const int row = 8 * (4 * q + (wave & 3)) + lr;
-    voff_a[q] = (uint32_t)row * (uint32_t)p.lda + (uint32_t)((ls ^ swz(row)) * 16);
-  }
-  uint32_t voff_w[C::kWPerWave];           // weight waves: rows (CW / 4) (wave - 4) + 8 i + lane / 8
-#pragma unroll
-  for (int i = 0; i < C::kWPerWave; ++i) {
-    const int row = (CW / 4) * (wave & 3) + 8 * i + lr;
-    voff_w[i] = (uint32_t)row * (uint32_t)p.ldb + (uint32_t)((ls ^ swz(row)) * 16);
+  for (int i = 0; i < kPer; ++i) {
+    const int row = 8 * (2 * i + h2) + lr;
+    voff[i] = (uint32_t)row * (uint32_t)(aload ? p.lda : p.ldb) + (uint32_t)((ls ^ swz(row)) * 16);
   }
 
   // One round of loads: activations (and their scales) of chunk ca into ring
@@ -213,28 +215,30 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
   // slot cw % kWStages. Chunks past the end load the last chunk again (into
   // slots no one reads any more), so every round issues the same loads.
   auto issue = [&](int ca, int cw) {
-    const int as = ca % C::kAStages, ws = cw % C::kWStages;
-    ca = min(ca, nc - 1);
-    cw = min(cw, nc - 1);
-    if (wave < 4) {
-      const u32x4 ra = make_rsrc(a_e + (int64_t)ca * BK, a_end);
-      const uint32_t abase = sbase + C::kAOff + as * C::kASlot;
-#pragma unroll
-      for (int q = 0; q < C::kAPerWave; ++q)
-        if (4 * q + wave < C::kAInstr) dma16_buf(ra, voff_a[q], abase + (4 * q + wave) * 8 * BK);
-      if (wave < C::kSaInstr) {
-        const float* s0 = sa_e + (int64_t)ca * p.ldsa;
-        const u32x4 rs = make_rsrc(reinterpret_cast<const uint8_t*>(s0), reinterpret_cast<const uint8_t*>(s0 + me));
-        dma4_buf(rs, (uint32_t)(64 * wave + lane) * 4u, sbase + C::kSaOff + as * C::kSaSlot + 64 * wave * 4);
-      }
-    } else {
+    if (wload) {
+      const int ws = cw % C::kWStages;
+      cw = min(cw, nc - 1);
       const u32x4 rw = make_rsrc(b_e + (int64_t)cw * BK, b_end);
       const uint32_t wbase = sbase + C::kWOff + ws * C::kWSlot;
 #pragma unroll
-      for (int i = 0; i < C::kWPerWave; ++i)
-        dma16_buf_nt(rw, voff_w[i], wbase + ((CW / 4) * (wave & 3) + 8 * i) * BK);
-      if (wave == 7) {
+      for (int i = 0; i < kWPer; ++i) dma16_buf_nt(rw, voff[i], wbase + (2 * i + h2) * 8 * BK);
+      if (wave == 5) {
         if (lane == 0) dma4(uniform_ptr(sb_e + cw), 0u, sbase + C::kSwOff + ws * 16);
+      }
+    } else if (aload) {
+      const int as = ca % C::kAStages;
+      ca = min(ca, nc - 1);
+      const u32x4 ra = make_rsrc(a_e + (int64_t)ca * BK, a_end);
+      const uint32_t abase = sbase + C::kAOff + as * C::kASlot;
+#pragma unroll
+      for (int i = 0; i < kAPer; ++i) dma16_buf(ra, voff[i], abase + (2 * i + h2) * 8 * BK);
+      const float* s0 = sa_e + (int64_t)ca * p.ldsa;
+      const u32x4 rs = make_rsrc(reinterpret_cast<const uint8_t*>(s0), reinterpret_cast<const uint8_t*>(s0 + me));
+#pragma unroll
+      for (int jj = 0; jj < C::kSaInstr; jj += 2) {
+        const int j = jj + h2;
+        if (j < C::kSaInstr)
+          dma4_buf(rs, (uint32_t)(64 * j + lane) * 4u, sbase + C::kSaOff + as * C::kSaSlot + 64 * j * 4);
       }
     }
   };
@@ -248,14 +252,18 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
   const int sw = swz(l16);
   const int off0 = l16 * BK + (((2 * lq) ^ sw) * 16);
   const int off1 = l16 * BK + (((2 * lq + 1) ^ sw) * 16);
-  // Row subtiles of this wave: 64-column shape rs(q) = 8 q + w against weight
-  // subtiles 0-3; 128-column shape rs(q) = 4 q + w / 2 against weight subtiles
-  // 4 (w % 2) .. 4 (w % 2) + 3. Subtiles at or past T are skipped (uniform
-  // per wave).
-  constexpr int kRowStep = C::kWide ? 4 : 8;
+  // Compute wave w (0-3). 128-column shape: the four weight subtiles of column
+  // half w % 2 against row subtiles rs(q) = w / 2 + 2 q; 64-column shape: all
+  // four weight subtiles against rs(q) = w + 4 q. Subtiles at or past T are
+  // skipped (uniform per wave; never the case for an even T in the 128-column
+  // shape or a T divisible by 4 in the 64-column one).
+  constexpr int kRowStep = C::kWide ? 2 : 4;
   constexpr int Q = (T + kRowStep - 1) / kRowStep;
+  constexpr bool kAllValid = T % kRowStep == 0;
+  const bool computes = wave < 4;
   const int rs0 = C::kWide ? (wave >> 1) : wave;
   const int cs0 = C::kWide ? 4 * (wave & 1) : 0;
+  auto valid = [&](int q) { return kAllValid || kRowStep * q + rs0 < T; };
   v4f acc[Q][4];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
@@ -266,16 +274,15 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
 #pragma clang loop unroll(disable)
   for (int c = 0; c < nc; ++c) {
     switch (wave) {   // uniform
-      case 0: wait_vmcnt<C::wait(0)>(); break;
-      case 1: wait_vmcnt<C::wait(1)>(); break;
-      case 2: wait_vmcnt<C::wait(2)>(); break;
-      case 3: wait_vmcnt<C::wait(3)>(); break;
+      case 4: wait_vmcnt<C::wait(4)>(); break;
+      case 5: wait_vmcnt<C::wait(5)>(); break;
+      case 6: wait_vmcnt<C::wait(6)>(); break;
       case 7: wait_vmcnt<C::wait(7)>(); break;
-      default: wait_vmcnt<C::wait(4)>(); break;
+      default: break;   // compute waves hold no loads
     }
     __syncthreads();
     issue(c + C::kAStages - 1, c + C::kWStages - 1);
-    if (rs0 < T) {
+    if (computes) {
       const uint8_t* as = smem + C::kAOff + (c % C::kAStages) * C::kASlot;
       const uint8_t* ws = smem + C::kWOff + (c % C::kWStages) * C::kWSlot;
       const float* sas = reinterpret_cast<const float*>(smem + C::kSaOff + (c % C::kAStages) * C::kSaSlot);
@@ -283,26 +290,31 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
       v8i wf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) wf[j] = frag(ws + 16 * (cs0 + j) * BK, off0, off1);
-      // all MFMAs of the chunk, then their folds (no branch between them, so
-      // the fragment reads and the MFMAs pipeline)
-      v4f pc[Q][4];
+      // two row subtiles at a time: their MFMAs, then their folds, so that no
+      // fold waits for the matrix unit and at most 8 results are live
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        if (kRowStep * q + rs0 < T) {
-          const v8i af = frag(as + 16 * (kRowStep * q + rs0) * BK, off0, off1);
+      for (int q0 = 0; q0 < Q; q0 += 2) {
+        v4f pc[2][4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pc[q][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af, zero, 0, 0, 0, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          const int q = q0 + u;
+          if (q < Q && valid(q)) {
+            const v8i af = frag(as + 16 * (kRowStep * q + rs0) * BK, off0, off1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              pc[u][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af, zero, 0, 0, 0, 0, 0, 0);
+          }
         }
-      }
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        if (kRowStep * q + rs0 < T) {
-          const float sc = sas[16 * (kRowStep * q + rs0) + l16] * swv;
+        for (int u = 0; u < 2; ++u) {
+          const int q = q0 + u;
+          if (q < Q && valid(q)) {
+            const float sc = sas[16 * (kRowStep * q + rs0) + l16] * swv;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[q][j][r] = __builtin_fmaf(pc[q][j][r], sc, acc[q][j][r]);
+              for (int r = 0; r < 4; ++r) acc[q][j][r] = __builtin_fmaf(pc[u][j][r], sc, acc[q][j][r]);
+          }
         }
       }
     }
@@ -311,11 +323,11 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if constexpr (!C::kWide) {
-    if (rs0 >= T) return;
+    if (!computes) return;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int r = 16 * (kRowStep * q + rs0) + l16;
-      if (kRowStep * q + rs0 < T && r < me) {
+      if (valid(q) && r < me) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + n0 + 16 * j + 4 * lq) = bf16x4(acc[q][j]);
@@ -351,7 +363,7 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int rs = kRowStep * q + rs0;
-        if (rs < t16) {
+        if (computes && rs < t16) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[q][j]), rm,
@@ -366,25 +378,32 @@ __device__ __forceinline__ void decode_slice(const DecodeArgs& p, uint8_t* smem,
       last = *flag == 1;
     }
     if (!last) return;                                 // uniform: the other half finishes the slice
-    const auto ro = region(1 - h);
-    v4f oth[Q][4];
+    if (computes) {
+      const auto ro = region(1 - h);
+      // four row subtiles at a time: all their loads, then their sums and stores
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int rs = kRowStep * q + rs0;
-      if (rs < t16) {
+      for (int q0 = 0; q0 < Q; q0 += 4) {
+        v4f oth[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          oth[q][j] = __builtin_bit_cast(
-              v4f, __builtin_amdgcn_raw_buffer_load_b128(ro, lane_off + (uint32_t)(8 * rs + cs0 + j) * 1024u, 0, kSc1));
-      }
-    }
+        for (int u = 0; u < 4; ++u) {
+          const int rs = kRowStep * (q0 + u) + rs0;
+          if (q0 + u < Q && rs < t16) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int r = 16 * (kRowStep * q + rs0) + l16;
-      if (kRowStep * q + rs0 < t16 && r < me) {
+            for (int j = 0; j < 4; ++j)
+              oth[u][j] = __builtin_bit_cast(
+                  v4f, __builtin_amdgcn_raw_buffer_load_b128(ro, lane_off + (uint32_t)(8 * rs + cs0 + j) * 1024u, 0, kSc1));
+          }
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + col + 16 * j) = bf16x4(acc[q][j] + oth[q][j]);
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u;
+          const int r = 16 * (kRowStep * q + rs0) + l16;
+          if (q < Q && kRowStep * q + rs0 < t16 && r < me) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<uint2*>(p.out + (int64_t)(m0 + r) * p.ldo + col + 16 * j) = bf16x4(acc[q][j] + oth[u][j]);
+          }
+        }
       }
     }
     if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
