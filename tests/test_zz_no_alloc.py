@@ -72,3 +72,41 @@ def test_noalloc_without_split_and_oversize():
         fb.fp8bq_grouped_gemm_decode_noalloc(8, [256 * e for e in range(9)], 4096, 7168, a.data_ptr(), 7168,
                                              sa.data_ptr(), 2048, b.data_ptr(), 7168, sb.data_ptr(), 56,
                                              out.data_ptr(), 4096, 0, sp)
+
+
+def test_noalloc_replays_in_a_captured_graph():
+    # the use it is for: captured once in a HIP graph (the first call, which
+    # takes the scratch's address, runs eagerly before the capture), replayed
+    # with eager work and synchronisations between replays; every replay must
+    # equal the eager result (the counters reset themselves, nothing is cleared
+    # by a memset node)
+    import torch
+    counts = [120, 75, 43, 10]
+    row_off = [0] + list(np.cumsum(counts))
+    G, m, n, k = len(counts), int(row_off[-1]), 512, 1536
+    a, sa, b, sb = _operands(204, counts, n, k)
+    out = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    ref = torch.empty_like(out)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fb.fp8bq_grouped_gemm_decode_noalloc(G, row_off, n, k, a.data_ptr(), k, sa.data_ptr(), m, b.data_ptr(), k,
+                                             sb.data_ptr(), k // 128, ref.data_ptr(), n, 0, s.cuda_stream)
+    s.synchronize()
+    log(f"[noalloc] graph capture, counts={counts}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fb.fp8bq_grouped_gemm_decode_noalloc(G, row_off, n, k, a.data_ptr(), k, sa.data_ptr(), m, b.data_ptr(), k,
+                                             sb.data_ptr(), k // 128, out.data_ptr(), n, 0,
+                                             torch.cuda.current_stream().cuda_stream)
+    for i in range(4):
+        out.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager result"
+        # eager work on the same scratch between replays
+        fb.fp8bq_grouped_gemm_decode_noalloc(G, row_off, n, k, a.data_ptr(), k, sa.data_ptr(), m, b.data_ptr(), k,
+                                             sb.data_ptr(), k // 128, out.data_ptr(), n, 0,
+                                             torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"eager call after replay {i} differs"
