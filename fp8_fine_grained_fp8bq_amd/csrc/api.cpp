@@ -95,7 +95,8 @@ int fp8bq_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx
     if (rows % 128) return fail(FP8BQ_E_SHAPE, "quant_act: column-wise mode needs rows (%lld) to be a multiple of 128", (long long)rows);
     if (ldq < rows) return fail(FP8BQ_E_INVAL, "quant_act: ldq < rows (transposed output)");
     if (lds < cols) return fail(FP8BQ_E_INVAL, "quant_act: lds < cols");
-    if (rows / 128 > 65535 || cols / 64 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
+    // grid: rows / 128 row blocks (x) by cols / 128 column blocks (y)
+    if (cols / 128 > 65535 || rows / 128 > ((int64_t)1 << 31) - 1) return fail(FP8BQ_E_SHAPE, "quant_act: too large");
   }
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))
     return fail(FP8BQ_E_ALIGN, "quant_act: x and q must be 16-byte aligned, s 4-byte aligned");

@@ -99,71 +99,75 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // 128x1 column-wise tiles, written transposed.
-// A 256-thread block stages 128 rows x 64 columns of bf16 in LDS. Thread t
-// then owns column pair p = t / 8 and rows [16 (t % 8), +16): it reduces both
-// columns' absmax with its 7 neighbours (one aligned group of 8 lanes), encodes
-// its 16 rows of each column and writes them as 16 contiguous bytes of the
-// transposed output, so each wave writes 128-byte runs of 16 output rows.
+// A 256-thread block stages 128 rows x 128 columns of bf16 (32 KB) in LDS: 16
+// lanes per row load its 256 bytes, eight rows apart 16 at a time, so each
+// thread has eight 16-byte loads in flight. Thread t then owns columns
+// 4 (t / 8) .. + 3 and rows [16 (t % 8), +16): it reduces each column's absmax
+// with its 7 neighbours (one aligned group of 8 lanes), encodes its 16 rows of
+// each column and writes them as 16 contiguous bytes of the transposed output,
+// so every output row of the block is one full 128-byte line. (Blocks of 64
+// columns staged dword by dword ran at 64% of 8 TB/s on X [16384, 7168].)
+// LDS: the 16-byte unit u (columns 8u .. 8u + 7) of staged row r sits at unit
+// u ^ (2 ((r / 16) % 8)). A column read (8 bytes per lane, 32 lanes: 4 column
+// quads of 8 rows 16 apart) then touches 16 distinct units, all 64 banks, and
+// a staging store (16 lanes on one row) 16 distinct units of that row.
 // ---------------------------------------------------------------------------
-constexpr int kColBlockCols = 64;
-constexpr int kColLdsStride = kColBlockCols / 2;       // dwords per staged row
-// Column pair c of staged row r sits at dword c ^ col_swz(r) of the row. A
-// staging store puts 4 rows x 8 column quads in one half-wave, and the column
-// reads put 8 row groups (16 rows apart) x 4 column pairs in one: with this
-// XOR each touches 32 distinct banks (a padded stride cannot do both: 16 rows
-// apart is a multiple of 16 banks for any odd stride).
-__device__ __forceinline__ int col_swz(int r) { return ((r >> 2) & 0x1C) | (r & 3); }
+__device__ __forceinline__ int cols_swz(int r) { return ((r >> 4) & 7) << 1; }
 
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
-  __shared__ uint32_t tile[128 * kColLdsStride];
+  __shared__ uint4 tile[128 * 16];   // 128 rows x 16 units of 16 bytes
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 128;
-  const int64_t c0 = (int64_t)blockIdx.x * kColBlockCols;
+  // row blocks vary fastest: consecutive blocks write neighbouring 128-byte
+  // pieces of the same transposed rows
+  const int64_t r0 = (int64_t)blockIdx.x * 128;
+  const int64_t c0 = (int64_t)blockIdx.y * 128;
+  const int l16 = t & 15, rs = t >> 4;
 
+  uint4 in[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = i * 32 + (t >> 3);
-    const int d = (t & 7) * 4;
-    const uint4 w = *reinterpret_cast<const uint4*>(x + (r0 + row) * ldx + c0 + d * 2);
-    uint32_t* dst = tile + row * kColLdsStride;
-    const int f = col_swz(row);
-    dst[(d + 0) ^ f] = w.x; dst[(d + 1) ^ f] = w.y; dst[(d + 2) ^ f] = w.z; dst[(d + 3) ^ f] = w.w;
-  }
+  for (int j = 0; j < 8; ++j)
+    in[j] = *reinterpret_cast<const uint4*>(x + (r0 + 16 * j + rs) * ldx + c0 + l16 * 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tile[(16 * j + rs) * 16 + (l16 ^ cols_swz(16 * j))] = in[j];
   __syncthreads();
 
   const int p = t >> 3, seg = t & 7;
-  uint32_t w[16];
-  uint32_t mlo = 0, mhi = 0;
+  const uint2* lt = reinterpret_cast<const uint2*>(tile);
+  uint2 w[16];
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    w[i] = tile[(seg * 16 + i) * kColLdsStride + (p ^ col_swz(seg * 16 + i))];
-    mlo = umax(mlo, w[i] & 0x7FFFu);
-    mhi = umax(mhi, (w[i] >> 16) & 0x7FFFu);
+    const int row = seg * 16 + i;
+    // columns 4p .. 4p + 3: half (p & 1) of logical unit p / 2
+    w[i] = lt[row * 32 + 2 * ((p >> 1) ^ cols_swz(row)) + (p & 1)];
+    m[0] = umax(m[0], w[i].x & 0x7FFFu);
+    m[1] = umax(m[1], (w[i].x >> 16) & 0x7FFFu);
+    m[2] = umax(m[2], w[i].y & 0x7FFFu);
+    m[3] = umax(m[3], (w[i].y >> 16) & 0x7FFFu);
   }
-  mlo = lane8_max(mlo);
-  mhi = lane8_max(mhi);
-  const TileScale slo = group_scale<POW2>(mlo), shi = group_scale<POW2>(mhi);
+  TileScale ts[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) ts[b] = group_scale<POW2>(lane8_max(m[b]));
 
-  uint4 clo, chi;
-  clo.x = encode4<POW2>(bf_lo(w[0]), bf_lo(w[1]), bf_lo(w[2]), bf_lo(w[3]), slo);
-  clo.y = encode4<POW2>(bf_lo(w[4]), bf_lo(w[5]), bf_lo(w[6]), bf_lo(w[7]), slo);
-  clo.z = encode4<POW2>(bf_lo(w[8]), bf_lo(w[9]), bf_lo(w[10]), bf_lo(w[11]), slo);
-  clo.w = encode4<POW2>(bf_lo(w[12]), bf_lo(w[13]), bf_lo(w[14]), bf_lo(w[15]), slo);
-  chi.x = encode4<POW2>(bf_hi(w[0]), bf_hi(w[1]), bf_hi(w[2]), bf_hi(w[3]), shi);
-  chi.y = encode4<POW2>(bf_hi(w[4]), bf_hi(w[5]), bf_hi(w[6]), bf_hi(w[7]), shi);
-  chi.z = encode4<POW2>(bf_hi(w[8]), bf_hi(w[9]), bf_hi(w[10]), bf_hi(w[11]), shi);
-  chi.w = encode4<POW2>(bf_hi(w[12]), bf_hi(w[13]), bf_hi(w[14]), bf_hi(w[15]), shi);
-
-  const int64_t col = c0 + 2 * p;
-  *reinterpret_cast<uint4*>(qt + col * ldq + r0 + seg * 16) = clo;
-  *reinterpret_cast<uint4*>(qt + (col + 1) * ldq + r0 + seg * 16) = chi;
+  auto col_value = [&](int i, int b) {
+    return b == 0 ? bf_lo(w[i].x) : b == 1 ? bf_hi(w[i].x) : b == 2 ? bf_lo(w[i].y) : bf_hi(w[i].y);
+  };
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint4 o;
+    o.x = encode4<POW2>(col_value(0, b), col_value(1, b), col_value(2, b), col_value(3, b), ts[b]);
+    o.y = encode4<POW2>(col_value(4, b), col_value(5, b), col_value(6, b), col_value(7, b), ts[b]);
+    o.z = encode4<POW2>(col_value(8, b), col_value(9, b), col_value(10, b), col_value(11, b), ts[b]);
+    o.w = encode4<POW2>(col_value(12, b), col_value(13, b), col_value(14, b), col_value(15, b), ts[b]);
+    *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldq + r0 + seg * 16) = o;
+  }
   if (seg == 0) {
-    float* sp = s + (int64_t)blockIdx.y * lds + col;
-    sp[0] = slo.s;
-    sp[1] = shi.s;
+    float* sp = s + (int64_t)blockIdx.x * lds + c0 + 4 * p;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sp[b] = ts[b].s;
   }
 }
 
@@ -644,7 +648,7 @@ hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 
 hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* qt, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st) {
-  dim3 grid((unsigned)(cols / kColBlockCols), (unsigned)(rows / 128));
+  dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 128));
   if (pow2)
     hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
   else

@@ -71,6 +71,11 @@ def test_quant_act_validation(L):
     col[6] = 200
     assert _st(L, f, *col) == fb.E_INVAL                                        # ldq < rows
     assert "ldq" in L.fp8bq_last_error().decode()
+    # col-wise grid: rows / 128 blocks along x, cols / 128 along y (at most 65535)
+    wide = 128 * 65536
+    assert _st(L, f, A16, 128, wide, wide, 1, B16, 128, S4, wide, None) == fb.E_SHAPE
+    assert "too large" in L.fp8bq_last_error().decode()
+    assert _st(L, f, A16, 128, wide - 128, wide - 128, 1, B16, 128, S4, wide, None) == fb.E_DEVICE
 
 
 def test_quant_w_validation(L):
