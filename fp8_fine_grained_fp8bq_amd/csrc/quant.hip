@@ -456,8 +456,32 @@ __device__ __forceinline__ uint32_t mag_max8(const uint4 a) {
   return umax(r.x, r.y);
 }
 
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Codes of two bf16 values (one dword w, magnitudes m = w & 0x7FFF7FFF) under
+// the tile scale 2^k, on the fast path: each value zero or, scaled, in E5M6's
+// normal range (bf16 exponent at least k + 113), and k >= -111. With a
+// power-of-two scale the code is then the bf16 magnitude with its lowest
+// mantissa bit rounded off (to nearest, ties to even; a carry moves into the
+// exponent) and the exponent rebiased by -(k + 112) (off = (k + 112) << 6 in
+// both halves); a zero gives a negative difference, clamped to 0, and the sign
+// bits move from bit 15 to bit 11. Two values per 32-bit instruction, with
+// packed 16-bit arithmetic. Returns the 24-bit group (low value in bits 0..11).
+__device__ __forceinline__ uint32_t e5m6_pair_fast(uint32_t w, uint32_t m, u16x2 off) {
+  const u16x2 q = __builtin_bit_cast(u16x2, m) >> (u16x2){1, 1};
+  const uint32_t tie = m & __builtin_bit_cast(uint32_t, q) & 0x00010001u;   // dropped bit 1 and q odd
+  const u16x2 cm = q + __builtin_bit_cast(u16x2, tie);
+  const i16x2 c = __builtin_elementwise_max(__builtin_bit_cast(i16x2, (u16x2)(cm - off)), (i16x2){0, 0});
+  const uint32_t code = __builtin_bit_cast(uint32_t, c) | ((w >> 4) & 0x08000800u);
+  return (code & 0x0FFFu) | ((code >> 4) & 0x00FFF000u);
+}
+
 // A thread takes NT neighbouring tiles of its row (NT = 2 when the row has an
 // even number of tiles: two loads in flight per lane, as in the FP8 kernel).
+// A wave whose values all qualify for e5m6_pair_fast (the usual case: E5M6
+// subnormals lie 28 binades below a tile's absmax) encodes them with it; any
+// other wave uses the general codec for that tile (half the VALU instructions
+// per value on the fast path, which ran the kernel at 73% of 8 TB/s before).
 template <int NT>
 __global__ __launch_bounds__(kRowThreads) void cache_e5m6_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int rows, int tpr, uint8_t* __restrict__ q, int64_t ldq,
@@ -475,11 +499,29 @@ __global__ __launch_bounds__(kRowThreads) void cache_e5m6_kernel(
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int k = e5m6_tile_exponent(row16_max(mag_max8(v[t])));
-    const float inv = exp2_int(-k);
     const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
-    uint32_t pr[4];   // element pairs (2i, 2i + 1) as 24-bit groups
+    uint32_t m[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = e5m6_code(bf_lo(w[i]) * inv) | (e5m6_code(bf_hi(w[i]) * inv) << 12);
+    for (int i = 0; i < 4; ++i) m[i] = w[i] & 0x7FFF7FFFu;
+    // fast path: every non-zero magnitude at least (k + 113) << 7 (m - 1 wraps a
+    // zero to 0xFFFF), k >= -111
+    const u16x2 one = {1, 1};
+    const u16x2 mn = __builtin_elementwise_min(
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, m[0]) - one, __builtin_bit_cast(u16x2, m[1]) - one),
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, m[2]) - one, __builtin_bit_cast(u16x2, m[3]) - one));
+    const uint32_t mn16 = mn.x < mn.y ? mn.x : mn.y;
+    const bool ok = k >= -111 && mn16 >= (uint32_t)(((k + 113) << 7) - 1);
+    uint32_t pr[4];   // element pairs (2i, 2i + 1) as 24-bit groups
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) {   // uniform per wave
+      const unsigned short o = (unsigned short)((k + 112) << 6);
+      const u16x2 off = {o, o};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = e5m6_pair_fast(w[i], m[i], off);
+    } else {
+      const float inv = exp2_int(-k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = e5m6_code(bf_lo(w[i]) * inv) | (e5m6_code(bf_hi(w[i]) * inv) << 12);
+    }
     if (r < rows) {
       *reinterpret_cast<uint3*>(q + (int64_t)row * ldq + (col0 + t) * 192 + l16 * 12) =
           make_uint3(pr[0] | (pr[1] << 24), (pr[1] >> 8) | (pr[2] << 16), (pr[2] >> 16) | (pr[3] << 8));
