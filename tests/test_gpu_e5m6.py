@@ -113,3 +113,34 @@ def test_edge_tiles():
 def test_dense_activation_full_size():
     cfg = dense_fprop()
     _assert_cache(cfg.x, name="dense X 4096x7168")
+
+
+def test_fast_path_boundaries():
+    # A wave covers 4 rows of one 128-column chunk; it encodes with the packed
+    # fast path only if every value is zero or has a bf16 magnitude at least
+    # (k + 113) << 7, and k >= -111. Rows 0-3: k = -111 tiles, all qualifying;
+    # rows 4-7: the same with one value a step below the threshold (the whole
+    # wave takes the general codec); rows 8-11: k = -112 tiles (general codec);
+    # rows 12-15: ordinary tiles with values exactly at the threshold, signed
+    # zeros and the tile maxima.
+    rng = np.random.default_rng(78)
+    x = np.zeros((16, 256), np.uint16)
+
+    def tile(amax_bits, lo_bits, n=128):
+        v = rng.integers(lo_bits, amax_bits + 1, n).astype(np.uint16)
+        v[0] = amax_bits
+        v |= (rng.integers(0, 2, n) << 15).astype(np.uint16)          # random signs
+        return v
+    for r in range(4):
+        x[r, :128] = tile(0x0F80, 0x0100)          # k = -111: threshold magnitude 0x0100
+        x[r, 128:] = tile(0x0FC0, 0x0100)
+    x[4:8] = x[0:4]
+    x[5, 17] = 0x00FF                               # one value just below the threshold
+    for r in range(8, 12):
+        x[r, :128] = tile(0x0F00, 0x0080)          # k = -112
+        x[r, 128:] = tile(0x0F7F, 0x0080)
+    for r in range(12, 16):
+        x[r, :128] = tile(0x3F80, 0x3100)          # amax 1.0: k = -15, threshold 0x3100
+        x[r, 128:] = tile(0x477E, 0x3800)          # amax 65024: k = 0, threshold 0x3880 -> values below it too
+    x[12, 1:9] = [0x3100, 0xB100, 0x0000, 0x8000, 0x3101, 0xB101, 0x3F80, 0xBF80]   # at the threshold, zeros
+    _assert_cache(x, name="fast path boundaries")
