@@ -179,7 +179,7 @@ def status_table(path):
 # kernels that --leg launches alone (each on the workload the bench times it on)
 LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "decode_fullk",
         "mfma_stream",
-        "cache_e5m6", "uncache_e5m6", "requant_e5m6")
+        "cache_e5m6", "uncache_e5m6", "requant_e5m6", "requant")
 
 
 def run_leg(args):
@@ -199,7 +199,7 @@ def run_leg(args):
     sp = torch.cuda.current_stream(dev).cuda_stream
     leg = args.leg
     cold = leg in ("quant_x", "quant_w", "qcol", "decode", "decode_fullk", "cache_e5m6", "uncache_e5m6",
-                   "requant_e5m6")
+                   "requant_e5m6", "requant")
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
     flops = nbytes = None
 
@@ -236,6 +236,22 @@ def run_leg(args):
             nbytes = M * (K * 3 // 2) + M * (K // 128) * 4 + K * M + (M // 128) * K * 4
             cache()
             fn = requant
+    elif leg == "requant":
+        # the power-of-two FP8 cache of X, re-quantised to transposed 128x1 tiles
+        cfg = workloads.large_fprop()
+        _, M, _, K = WORKLOADS["large"]
+        x = dev16(cfg.x)
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        xqt = torch.empty((K, M), dtype=torch.uint8, device=dev)
+        xst = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+        fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | fb.SCALE_POW2, xq.data_ptr(), K,
+                                 xs.data_ptr(), M, sp)
+        nbytes = 2 * M * K + 2 * (M * (K // 128) * 4)
+
+        def fn():
+            fb.fp8bq_requant_t_128x1(xq.data_ptr(), M, K, K, xs.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(), K,
+                                     0, sp)
     elif leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
         cfg = workloads.large_fprop()
         _, M, N, K = WORKLOADS["large"]
