@@ -179,7 +179,7 @@ def status_table(path):
 # kernels that --leg launches alone (each on the workload the bench times it on)
 LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "decode_fullk",
         "mfma_stream",
-        "cache_e5m6", "uncache_e5m6", "requant_e5m6", "requant")
+        "cache_e5m6", "uncache_e5m6", "requant_e5m6", "requant", "grouped")
 
 
 def run_leg(args):
@@ -252,6 +252,25 @@ def run_leg(args):
         def fn():
             fb.fp8bq_requant_t_128x1(xq.data_ptr(), M, K, K, xs.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(), K,
                                      0, sp)
+    elif leg == "grouped":
+        # MoE grouped Fprop: 8 local experts, Zipf top-8 routing, rows padded to 128
+        moe = workloads.moe_fprop()
+        G_m, N_m, K_m = moe.w.shape
+        m_m = int(moe.row_off[-1])
+        g_xq, g_xs = fb.quant_act_1x128(dev16(moe.x))
+        g_wq = torch.empty((G_m, N_m, K_m), dtype=torch.uint8, device=dev)
+        g_ws = torch.empty((G_m, N_m // 128, K_m // 128), dtype=torch.float32, device=dev)
+        for e in range(G_m):
+            q_e, s_e, _ = fb.quant_w_128x128(dev16(moe.w[e]))
+            g_wq[e].copy_(q_e)
+            g_ws[e].copy_(s_e)
+        g_y = torch.empty((m_m, N_m), dtype=torch.bfloat16, device=dev)
+        g_off = [int(v) for v in moe.row_off]
+        flops = 2.0 * float(np.sum(moe.real_rows)) * N_m * K_m
+
+        def fn():
+            fb.fp8bq_grouped_gemm(G_m, g_off, N_m, K_m, g_xq.data_ptr(), K_m, g_xs.data_ptr(), m_m, g_wq.data_ptr(),
+                                  K_m, g_ws.data_ptr(), K_m // 128, g_y.data_ptr(), N_m, 0, sp)
     elif leg in ("fprop", "fprop_pow2", "quant_x", "quant_w"):
         cfg = workloads.large_fprop()
         _, M, N, K = WORKLOADS["large"]

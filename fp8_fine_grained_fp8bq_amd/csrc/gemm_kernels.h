@@ -298,38 +298,50 @@ __device__ __forceinline__ uint2 pack_bf16x4(const v4f& v) {
 // cost per active lane, so 16-byte lanes halve the epilogue's store work.
 // Returns the 16 bytes; they go to the lane's own column of subtile j (even
 // lanes) or 12 columns on from it (odd lanes).
-__device__ __forceinline__ uint4 pair16(uint2 A, uint2 B, bool odd) {
-  const uint2 snd = odd ? A : B;
-  uint2 rcv;
-  rcv.x = (uint32_t)__shfl_xor((int)snd.x, 16);
-  rcv.y = (uint32_t)__shfl_xor((int)snd.y, 16);
-  return odd ? make_uint4(rcv.x, rcv.y, B.x, B.y) : make_uint4(A.x, A.y, rcv.x, rcv.y);
+// v_permlane16_swap_b32 (gfx950) exchanges the odd 16-lane rows of its first
+// operand with the even rows of its second: with A first and B second, even
+// rows end with (own A, partner's A) and odd rows with (partner's B, own B),
+// which is the regrouping itself, with no lane index, select or LDS crossbar.
+__device__ __forceinline__ uint4 pair16(uint2 A, uint2 B) {
+  const auto x = __builtin_amdgcn_permlane16_swap(A.x, B.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(A.y, B.y, false, false);
+  return make_uint4(x[0], y[0], x[1], y[1]);
+}
+
+// The lane's index within its wave, recomputed where it is used: the inline
+// asm cannot be moved or merged, so the compiler does not hoist lane-dependent
+// epilogue and tile-change offsets out of the K-loop and keep them live through
+// it (the 256-column kernels spilled them to scratch, and every reload waited
+// for all loads in flight).
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // The codes of four subtiles of one output row (d[k]: columns 16 k + 4 lq ..
 // 16 k + 4 lq + 3 of subtile group g, from lane lq of the row) transposed
-// between the row's four lanes (two exchange rounds, partners lq ^ 1 and
-// lq ^ 2): lane lq ends with the 16 codes of subtile 4 g + lq, one 16-byte
-// store instead of four 4-byte ones.
-__device__ __forceinline__ uint4 codes16(const uint32_t (&d)[4], int lq) {
-  const bool b0 = (lq & 1) != 0, b1 = (lq & 2) != 0;
-  // round 1: keep the dwords whose index has bit 0 = b0, swap the others
-  const uint32_t s0 = b0 ? d[0] : d[1], s1 = b0 ? d[2] : d[3];
-  const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 16), r1 = (uint32_t)__shfl_xor((int)s1, 16);
-  const uint32_t own_lo = b0 ? d[1] : d[0], own_hi = b0 ? d[3] : d[2];
-  // now: own_lo / own_hi = this lane's index b0 / b0 + 2, r0 / r1 the partner's
-  // round 2: keep index lq (= b0 + 2 b1), swap index lq ^ 2
-  const uint32_t x_keep = b1 ? own_hi : own_lo, y_keep = b1 ? r1 : r0;
-  const uint32_t x_send = b1 ? own_lo : own_hi, y_send = b1 ? r0 : r1;
-  const uint32_t rx = (uint32_t)__shfl_xor((int)x_send, 32), ry = (uint32_t)__shfl_xor((int)y_send, 32);
-  // source lanes: lq (x_keep), lq ^ 1 (y_keep), lq ^ 2 (rx), lq ^ 3 (ry)
-  uint32_t o[4];
-#pragma unroll
-  for (int src = 0; src < 4; ++src) {
-    const int rel = src ^ lq;
-    o[src] = rel == 0 ? x_keep : rel == 1 ? y_keep : rel == 2 ? rx : ry;
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+// between the row's four lanes, which sit in the wave's four 16-lane rows:
+// lane lq ends with the 16 codes of subtile 4 g + lq, one 16-byte store
+// instead of four 4-byte ones. Two v_permlane16_swap_b32 (odd rows of the first
+// operand <-> even rows of the second) leave every lane with index lq & 1 of
+// both lanes of its row pair, for subtiles lq & 1 and 2 + (lq & 1); two
+// v_permlane32_swap_b32 (rows 2, 3 of the first <-> rows 0, 1 of the second)
+// then bring the other pair's values, in source-lane order on every lane.
+__device__ __forceinline__ uint4 codes16(const uint32_t (&d)[4]) {
+  const auto xy = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+  const auto zw = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+  const auto p0 = __builtin_amdgcn_permlane32_swap(xy[0], zw[0], false, false);
+  const auto p1 = __builtin_amdgcn_permlane32_swap(xy[1], zw[1], false, false);
+  return make_uint4(p0[0], p1[0], p0[1], p1[1]);
+}
+
+// Largest of a value over the four lanes l16 + 16 lq of an output row.
+__device__ __forceinline__ uint32_t row_max4(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umax(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax(b[0], b[1]);
 }
 
 // Stores a wave's TM x TN subtiles (lane: output row l16 of subtile i, columns
@@ -338,7 +350,7 @@ __device__ __forceinline__ uint4 codes16(const uint32_t (&d)[4], int lq) {
 // check every row and column.
 template <int KIND, int TM, int TN, int TBN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, const v4f (&acc)[TM][TN],
-                                           int64_t row0, int64_t col0) {
+                                           int64_t row0, int64_t col0, int lq) {
   auto put = [&](int64_t row, int64_t col, const v4f& v) {
     if constexpr (KIND == KIND_WGRAD) {
       *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + row * p.ldo + col) = v;
@@ -353,12 +365,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& cur, c
 #pragma unroll
         for (int j = 0; j < TN; ++j) put(row0 + i * 16, col0 + j * 16, acc[i][j]);
     } else {
-      const bool odd = ((threadIdx.x >> 4) & 1) != 0;
+      const bool odd = (lq & 1) != 0;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int jp = 0; jp < TN / 2; ++jp) {
-          const uint4 v = pair16(pack_bf16x4(acc[i][2 * jp]), pack_bf16x4(acc[i][2 * jp + 1]), odd);
+          const uint4 v = pair16(pack_bf16x4(acc[i][2 * jp]), pack_bf16x4(acc[i][2 * jp + 1]));
           const int64_t col = col0 + 2 * jp * 16 + (odd ? 12 : 0);
           *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (row0 + i * 16) * p.ldo + col) = v;
         }
@@ -405,8 +417,7 @@ __device__ __forceinline__ void store_tile_q(const GemmArgs& p, const Tile& cur,
       __builtin_memcpy(&w[j].y, &hi, 4);
       amax = umax(amax, umax(mag_max2(w[j].x), mag_max2(w[j].y)));
     }
-    amax = umax(amax, (uint32_t)__shfl_xor((int)amax, 16));
-    amax = umax(amax, (uint32_t)__shfl_xor((int)amax, 32));
+    amax = row_max4(amax);
     const TileScale ts = group_scale<POW2>(amax);
     uint32_t code[TN];
 #pragma unroll
@@ -417,11 +428,11 @@ __device__ __forceinline__ void store_tile_q(const GemmArgs& p, const Tile& cur,
 #pragma unroll
     for (int g = 0; g < TN / 4; ++g) {
       const uint32_t d[4] = {code[4 * g], code[4 * g + 1], code[4 * g + 2], code[4 * g + 3]};
-      c16[g] = codes16(d, lq);
+      c16[g] = codes16(d);
     }
     if (bf_out) {
 #pragma unroll
-      for (int jp = 0; jp < TN / 2; ++jp) b16[jp] = pair16(w[2 * jp], w[2 * jp + 1], (lq & 1) != 0);
+      for (int jp = 0; jp < TN / 2; ++jp) b16[jp] = pair16(w[2 * jp], w[2 * jp + 1]);
     }
     if (row < cur.m_end) {
       const int64_t gcol = col0 - 4 * lq;       // the wave's first column
@@ -446,7 +457,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& cur, con
                                          int64_t row0, int64_t n_wave, int lq) {
   static_assert(QMODE == 0 || TBN == BN, "quantised output: 256-column tiles");
   if constexpr (QMODE == 0)
-    store_tile<KIND, TM, TN, TBN>(p, cur, acc, row0, n_wave + 4 * lq);
+    store_tile<KIND, TM, TN, TBN>(p, cur, acc, row0, n_wave + 4 * lq, lq);
   else
     store_tile_q<QMODE == 2, TM, TN>(p, cur, acc, row0, n_wave + 4 * lq, n_wave / 128, lq);
 }
@@ -521,23 +532,24 @@ struct Loader {
 
   __device__ __forceinline__ void cursor_tile() {
     const Tile t = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * dtk);
+    const int ln = lane_fresh();   // not `lane`: its 64-bit offsets would be kept live through the K-loop
     rs_a = make_rsrc(p.a + t.m0 * p.lda, p.a + (p.m - 1) * p.lda + p.k);
     rs_b = make_rsrc(t.b + t.n0 * p.ldb, t.b + (p.n - 1) * p.ldb + p.k);
 #pragma unroll
     for (int v = 0; v < kScaleWaves; ++v) {
       const int sw = wave + v * WAVES, q4 = sw & 3;
       if (sw < 4) {
-        s_off[v] = (uint32_t)(min(t.m0 + 64 * q4 + lane, t.m_end - 1) - t.m0) * 4u;
+        s_off[v] = (uint32_t)(min(t.m0 + 64 * q4 + ln, t.m_end - 1) - t.m0) * 4u;
         d_sk[v] = p.sa + t.m0;
       } else if constexpr (KIND == KIND_WGRAD) {
-        s_off[v] = (uint32_t)(min(t.n0 + 64 * q4 + lane, t.n_end - 1) - t.n0) * 4u;
+        s_off[v] = (uint32_t)(min(t.n0 + 64 * q4 + ln, t.n_end - 1) - t.n0) * 4u;
         d_sk[v] = t.sb + t.n0;
       } else {
           // the tile's columns span blocks blk0 .. blk0 + last (last <= 2): lane l
         // brings block blk0 + min(l, last)
         const int64_t blk0 = t.n0 / 128;
         const int64_t last = (t.n_end - 1) / 128 - blk0;
-        const int64_t bsel = TBN % 128 == 0 ? (lane < 1 ? 0 : last) : min((int64_t)lane, last);
+        const int64_t bsel = TBN % 128 == 0 ? (ln < 1 ? 0 : last) : min((int64_t)ln, last);
         s_off[v] = (uint32_t)(KIND == KIND_FPROP ? bsel * p.ldsb : bsel) * 4u;
         d_sk[v] = KIND == KIND_FPROP ? t.sb + blk0 * p.ldsb : t.sb + blk0;
       }
@@ -609,7 +621,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
 
   const Walk wk = make_walk(p);
   if (wk.my_tiles == 0) return;                                // uniform: no tile for this workgroup
-  const int my_tiles = wk.my_tiles, nc = wk.nc, total = wk.total;
+  const int my_tiles = wk.my_tiles, nc = wk.nc;
   Loader<KIND, GROUPED, C::kWaves, LOADERS, TBN> ld(p, g, wk, lds_addr(smem), wave, lane);
   constexpr int kParts = decltype(ld)::kParts;
 
@@ -817,7 +829,9 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) scp[i] = 0.f;
     const Tile cur = make_tile<GROUPED, TBN>(p, g, wk.start + wk.local + wk.nper * tk);
-    epilogue<KIND, QMODE, C::TM, C::TN, TBN>(p, cur, acc, cur.m0 + wave_m * C::WM + l16, cur.n0 + wave_n * C::WN, lq);
+    const int el = lane_fresh();
+    epilogue<KIND, QMODE, C::TM, C::TN, TBN>(p, cur, acc, cur.m0 + wave_m * C::WM + (el & 15), cur.n0 + wave_n * C::WN,
+                                             el >> 4);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -1053,7 +1067,8 @@ __global__ __launch_bounds__(256) void gemm_pow2_kernel(GemmArgs p, GroupArgs g)
 
     // ---- tile done: epilogue --------------------------------------------------
     const Tile cur = make_tile<GROUPED>(p, g, wk.start + wk.local + wk.nper * tk);
-    epilogue<KIND, QMODE, TM, TN>(p, cur, acc, cur.m0 + wave_m * WM + l16, cur.n0 + wave_n * WN, lq);
+    const int el = lane_fresh();
+    epilogue<KIND, QMODE, TM, TN>(p, cur, acc, cur.m0 + wave_m * WM + (el & 15), cur.n0 + wave_n * WN, el >> 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
