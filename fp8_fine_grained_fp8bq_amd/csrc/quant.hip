@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
 // integral power of two (section 3.3.3), so the conversion adds no error of its
 // own where the row scale is not below the new one.
 // x_hat = dec(q) * s is formed in float64, where it is exact for any binary32
-// scale (4 + 24 significant bits); the new scale is 2^k with k the smallest
+// scale (4 + 24 significant bits), or in binary32 where that is exact too (see
+// the kernel); the new scale is 2^k with k the smallest
 // exponent such that the 128x1 group's absmax is at most 448 * 2^k (E8M0
 // range, 2^-127 for an all-zero group); the code is E4M3(fl32(x_hat * 2^-k)),
 // the product exact in float64 and rounded once to binary32.
@@ -187,8 +188,15 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
 // in LDS; thread (p, seg) takes columns 4p .. 4p + 3 of rows 16 seg .. 16 seg +
 // 15, so each of its four output rows gets 16 consecutive bytes; the column
 // maxima meet across the 8 lanes that share p.
+// LDS: staged row r at 128 r bytes; its 16-byte unit u (codes 16u .. 16u + 15)
+// sits at unit u ^ ((r / 16) % 8). A column read (one dword per lane; over 32
+// lanes p takes four consecutive values within one unit and seg 0..7) then
+// touches 32 distinct dwords of one 128-byte stripe of banks, and a staging
+// store (8 lanes on one row) the 8 units of that row. (Rows padded to 33
+// dwords instead put rows 16 seg and 16 (seg + 4) on the same banks: a 2-way
+// conflict in every read.)
 // ---------------------------------------------------------------------------
-constexpr int kReqStride = 33;   // dwords per staged row of 128 codes (+1 pad)
+__device__ __forceinline__ int req_unit(int u, int r) { return u ^ ((r >> 4) & 7); }
 
 // The four E4M3 codes of a word as floats (exact; hardware conversion).
 __device__ __forceinline__ void dec4(uint32_t w, float (&f)[4]) {
@@ -198,10 +206,36 @@ __device__ __forceinline__ void dec4(uint32_t w, float (&f)[4]) {
   f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
 }
 
+// A 64-bit value moved between lanes by one DPP pattern (both halves alike).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t b) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest of a non-negative double over an aligned group of 8 lanes. For
+// non-negative doubles the order is that of their bit patterns as unsigned
+// integers, so the rounds of lane8_max (partners lane ^ 1, lane ^ 2, then the
+// group's mirror) apply to the patterns, in VALU and DPP instead of the LDS
+// crossbar.
 __device__ __forceinline__ double dmax_lane8(double v) {
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) v = fmax(v, __shfl_xor(v, m, 64));
-  return v;
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  uint64_t o = dpp_u64<0xB1>(b);
+  b = o > b ? o : b;
+  o = dpp_u64<0x4E>(b);
+  b = o > b ? o : b;
+  o = dpp_u64<0x141>(b);
+  b = o > b ? o : b;
+  return __longlong_as_double((long long)b);
+}
+
+// The same for a binary32 a >= 0: a = 1.f * 2^(E - 127) with 448 = 1.75 * 2^8
+// (a zero or subnormal a gives k <= -134, clamped to -127, as in float64).
+__device__ __forceinline__ int pow2_exponent_f32(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int k = (int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(-127, min(127, k));
 }
 
 // k = smallest integer with a <= 448 * 2^k, clamped to [-127, 127]; a >= 0.
@@ -216,7 +250,7 @@ __device__ __forceinline__ int pow2_exponent_f64(double a) {
 __global__ __launch_bounds__(256) void requant_t_kernel(
     const uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
-  __shared__ uint32_t tile[128 * kReqStride];
+  __shared__ uint4 tile[128 * 8];   // 128 rows x 8 units of 16 bytes
   const int t = threadIdx.x;
   // row blocks vary fastest: consecutive blocks write neighbouring 128-byte
   // pieces of the same transposed rows (6% faster than column blocks fastest)
@@ -225,9 +259,8 @@ __global__ __launch_bounds__(256) void requant_t_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = i * 32 + (t >> 3);
-    const uint4 w = *reinterpret_cast<const uint4*>(q + (r0 + row) * ldq + c0 + (t & 7) * 16);
-    uint32_t* dst = tile + row * kReqStride + (t & 7) * 4;
-    dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+    tile[row * 8 + req_unit(t & 7, row)] =
+        *reinterpret_cast<const uint4*>(q + (r0 + row) * ldq + c0 + (t & 7) * 16);
   }
   const int p = t >> 3, seg = t & 7;
   const float* srow = s + (int64_t)blockIdx.y * lds + r0 + seg * 16;
@@ -236,38 +269,73 @@ __global__ __launch_bounds__(256) void requant_t_kernel(
   for (int i = 0; i < 16; ++i) sf[i] = srow[i];
   __syncthreads();
 
-  // pass 1: the column maxima of |x_hat|; pass 2 forms x_hat again (cheaper
-  // than keeping 64 float64 values live)
   uint32_t w[16];
-  double cmax[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    w[i] = tile[(seg * 16 + i) * kReqStride + p];
-    float d[4];
-    dec4(w[i], d);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) cmax[b] = fmax(cmax[b], fabs((double)d[b] * (double)sf[i]));   // exact
-  }
-  int k[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) k[b] = pow2_exponent_f64(dmax_lane8(cmax[b]));
+  for (int i = 0; i < 16; ++i)   // dword p of row 16 seg + i: dword p % 4 of logical unit p / 4
+    w[i] = reinterpret_cast<const uint32_t*>(tile)[(seg * 16 + i) * 32 + req_unit(p >> 2, seg * 16) * 4 + (p & 3)];
 
-  float v[4][16];
+  // Row scales that are powers of two 2^e with -117 <= e <= 118 (the forward
+  // pass's activation scales, report section 3.3.3): dec(q) * s then has at
+  // most 4 significant bits and lies in binary32's normal range (|dec(q)| <=
+  // 448 < 2^9, and its smallest nonzero magnitude 2^-9 times 2^-117 is
+  // 2^-126), so binary32 forms x_hat exactly, and with it the column maxima
+  // and x_hat * 2^-k (exact, or below 2^-126, where it encodes to a signed
+  // zero whether rounded or flushed): the float64 path's values, at a fraction
+  // of its cost. A wave takes this path when every lane's scales qualify.
+  bool fast = true;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float d[4];
-    dec4(w[i], d);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) v[b][i] = (float)ldexp((double)d[b] * (double)sf[i], -k[b]);   // exact, one rounding
+    const uint32_t b = __float_as_uint(sf[i]);
+    fast = fast && (b & 0x807FFFFFu) == 0u && (b >> 23) - 10u <= 235u;   // exponent field 10 .. 245
   }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  // Output row b of the thread (column 4p + b) is byte b of every w[i]: it is
+  // formed and encoded four values at a time, so only w, sf and four codes are
+  // live (all 64 values at once would take most of the register file).
+  auto emit = [&](int b, auto&& value) {
     uint4 o;
-    o.x = cvt4(v[b][0], v[b][1], v[b][2], v[b][3]);
-    o.y = cvt4(v[b][4], v[b][5], v[b][6], v[b][7]);
-    o.z = cvt4(v[b][8], v[b][9], v[b][10], v[b][11]);
-    o.w = cvt4(v[b][12], v[b][13], v[b][14], v[b][15]);
+    uint32_t* const op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      op[g] = cvt4(value(4 * g, b), value(4 * g + 1, b), value(4 * g + 2, b), value(4 * g + 3, b));
     *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldqt + r0 + seg * 16) = o;
+  };
+  auto dec1 = [&](int i, int b) {   // (b is a constant once unrolled: one conversion)
+    const int x = (int)w[i];
+    return b == 0 ? __builtin_amdgcn_cvt_f32_fp8(x, 0) : b == 1 ? __builtin_amdgcn_cvt_f32_fp8(x, 1)
+         : b == 2 ? __builtin_amdgcn_cvt_f32_fp8(x, 2) : __builtin_amdgcn_cvt_f32_fp8(x, 3);
+  };
+  int k[4];
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0) {   // wave-uniform
+    float cmax[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float d[4];
+      dec4(w[i], d);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cmax[b] = fmaxf(cmax[b], fabsf(d[b] * sf[i]));   // exact
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      k[b] = pow2_exponent_f32(__uint_as_float(lane8_max(__float_as_uint(cmax[b]))));
+      emit(b, [&](int i, int bb) { return ldexpf(dec1(i, bb) * sf[i], -k[bb]); });
+    }
+  } else {
+    // pass 1: the column maxima of |x_hat|; pass 2 forms x_hat again (cheaper
+    // than keeping 64 float64 values live)
+    double cmax[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float d[4];
+      dec4(w[i], d);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cmax[b] = fmax(cmax[b], fabs((double)d[b] * (double)sf[i]));   // exact
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      k[b] = pow2_exponent_f64(dmax_lane8(cmax[b]));
+      // exact product, one rounding
+      emit(b, [&](int i, int bb) { return (float)ldexp((double)dec1(i, bb) * (double)sf[i], -k[bb]); });
+    }
   }
   if (seg == 0) {
     float4 sc;

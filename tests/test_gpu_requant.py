@@ -76,6 +76,24 @@ def test_every_code_and_extreme_scales():
     _check(q, s, "all codes, scales 2^-127 .. 2^127")
 
 
+def test_fast_path_scale_bounds():
+    # the kernel forms x_hat in binary32 when all 128 row scales of a block are
+    # 2^e with -117 <= e <= 118, else in float64: blocks at both bounds and just
+    # past them, a block mixing the two bounds (its small rows far below the
+    # column maxima), and one whose single out-of-range row sends it to float64
+    rng = np.random.default_rng(40)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    exps = [[-117], [-118], [118], [119], [-117, 118], [0] * 127 + [-118]]
+    rows, cols = 128 * len(exps), 256
+    q = codes[rng.integers(0, codes.size, (rows, cols))]
+    q[::7, :] = 0x7E                              # +448 in every column of some rows
+    k = np.zeros((rows, cols // 128), np.int32)
+    for b, e in enumerate(exps):
+        k[b * 128:(b + 1) * 128] = np.resize(np.array(e, np.int32), 128)[:, None]
+    s = np.ldexp(np.float32(1.0), k).astype(np.float32)
+    _check(q, s, "scales at the binary32 path's bounds")
+
+
 def test_general_scales_rounding():
     # scales that are not powers of two: x_hat needs up to 28 bits, the new
     # codes come from one binary32 rounding of x_hat * 2^-k
