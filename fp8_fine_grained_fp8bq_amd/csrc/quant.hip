@@ -108,11 +108,14 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 // so every output row of the block is one full 128-byte line. (Blocks of 64
 // columns staged dword by dword ran at 64% of 8 TB/s on X [16384, 7168].)
 // LDS: the 16-byte unit u (columns 8u .. 8u + 7) of staged row r sits at unit
-// u ^ (2 ((r / 16) % 8)). A column read (8 bytes per lane, 32 lanes: 4 column
-// quads of 8 rows 16 apart) then touches 16 distinct units, all 64 banks, and
-// a staging store (16 lanes on one row) 16 distinct units of that row.
+// u ^ ((r / 16) % 8). The LDS serves 128 bytes per clock, 16 lanes of an
+// 8-byte read or 8 lanes of a 16-byte store at a time; a column read (16
+// lanes: 2 column quads of 8 rows 16 apart) then touches 16 distinct 8-byte
+// pieces of a 128-byte stripe, and a staging store (8 lanes on one row) 8
+// distinct units. (XOR by twice the row group, as first written, let row groups
+// g and g + 4 collide within 128 bytes: a 2-way conflict in every read.)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int cols_swz(int r) { return ((r >> 4) & 7) << 1; }
+__device__ __forceinline__ int cols_swz(int r) { return (r >> 4) & 7; }
 
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
@@ -141,8 +144,9 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = seg * 16 + i;
-    // columns 4p .. 4p + 3: half (p & 1) of logical unit p / 2
-    w[i] = lt[row * 32 + 2 * ((p >> 1) ^ cols_swz(row)) + (p & 1)];
+    // columns 4p .. 4p + 3: half (p & 1) of logical unit p / 2, i.e. 8-byte
+    // piece 2 ((p / 2) ^ g) + (p & 1) = p ^ 2 g
+    w[i] = lt[row * 32 + (p ^ (2 * cols_swz(row)))];
     m[0] = umax(m[0], w[i].x & 0x7FFFu);
     m[1] = umax(m[1], (w[i].x >> 16) & 0x7FFFu);
     m[2] = umax(m[2], w[i].y & 0x7FFFu);
