@@ -179,7 +179,7 @@ def status_table(path):
 # kernels that --leg launches alone (each on the workload the bench times it on)
 LEGS = ("fprop", "fprop_pow2", "quant_x", "quant_w", "dense", "dgrad", "wgrad", "qcol", "decode", "decode_fullk",
         "mfma_stream",
-        "cache_e5m6", "uncache_e5m6", "requant_e5m6", "requant", "grouped")
+        "cache_e5m6", "uncache_e5m6", "requant_e5m6", "requant", "requant_exact", "grouped")
 
 
 def run_leg(args):
@@ -199,7 +199,7 @@ def run_leg(args):
     sp = torch.cuda.current_stream(dev).cuda_stream
     leg = args.leg
     cold = leg in ("quant_x", "quant_w", "qcol", "decode", "decode_fullk", "cache_e5m6", "uncache_e5m6",
-                   "requant_e5m6", "requant")
+                   "requant_e5m6", "requant", "requant_exact")
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) if cold else None
     flops = nbytes = None
 
@@ -236,8 +236,9 @@ def run_leg(args):
             nbytes = M * (K * 3 // 2) + M * (K // 128) * 4 + K * M + (M // 128) * K * 4
             cache()
             fn = requant
-    elif leg == "requant":
-        # the power-of-two FP8 cache of X, re-quantised to transposed 128x1 tiles
+    elif leg in ("requant", "requant_exact"):
+        # the power-of-two (or, requant_exact, the absmax/448) FP8 cache of X,
+        # re-quantised to transposed 128x1 tiles
         cfg = workloads.large_fprop()
         _, M, _, K = WORKLOADS["large"]
         x = dev16(cfg.x)
@@ -245,13 +246,13 @@ def run_leg(args):
         xs = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
         xqt = torch.empty((K, M), dtype=torch.uint8, device=dev)
         xst = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
-        fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | fb.SCALE_POW2, xq.data_ptr(), K,
-                                 xs.data_ptr(), M, sp)
+        fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | (0 if leg == "requant_exact" else fb.SCALE_POW2),
+                                 xq.data_ptr(), K, xs.data_ptr(), M, sp)
         nbytes = 2 * M * K + 2 * (M * (K // 128) * 4)
 
         def fn():
             fb.fp8bq_requant_t_128x1(xq.data_ptr(), M, K, K, xs.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(), K,
-                                     0, sp)
+                                     0 if leg == "requant_exact" else fb.SCALE_POW2, sp)
     elif leg == "grouped":
         # MoE grouped Fprop: 8 local experts, Zipf top-8 routing, rows padded to 128
         moe = workloads.moe_fprop()
@@ -644,21 +645,26 @@ def main():
     tg_p2 = st_tg_p2["mean"]
     log(f"[bench] power-of-two scales: {ms_step_p2:.3f} ms/step, GEMM {tg_p2:.1f} us")
 
-    # transposing re-quantisation (1x128 -> 128x1) of the power-of-two cache of X
-    # that step_p2 left in xq / xs
+    # transposing re-quantisation (1x128 -> 128x1) of the power-of-two cache of X,
+    # in buffers of its own (time_kernel's settling steps rewrite xq / xs with
+    # the absmax/448 cache)
+    xq_c = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs_c = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    fb.fp8bq_quant_act_1x128(x.data_ptr(), M, K, K, fb.ACT_ROWWISE | fb.SCALE_POW2, xq_c.data_ptr(), K,
+                             xs_c.data_ptr(), M, sp)
     xqt = torch.empty((K, M), dtype=torch.uint8, device=dev)
     xst = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
 
     def requant():
-        fb.fp8bq_requant_t_128x1(xq.data_ptr(), M, K, K, xs.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(), K,
-                                 0, sp)
+        fb.fp8bq_requant_t_128x1(xq_c.data_ptr(), M, K, K, xs_c.data_ptr(), M, xqt.data_ptr(), M, xst.data_ptr(),
+                                 K, fb.SCALE_POW2, sp)
 
     requant()
     st_t_rq = time_kernel(requant, args.kernel_reps, True)
     t_rq = st_t_rq["mean"]
     bytes_rq = 2 * M * K + 2 * (M * (K // 128) * 4)
     log(f"[bench] requant 1x128 -> 128x1: {t_rq:.1f} us ({bytes_rq / t_rq / 1e3:.0f} GB/s)")
-    del xqt, xst
+    del xqt, xst, xq_c, xs_c
 
     # E5M6 activation cache of X (1x128 tiles, power-of-two scales, 12-bit codes
     # packed two per 3 bytes) and its inverse, both cold

@@ -259,10 +259,11 @@ def requant_e5m6_t_128x1(q, s, cols):
     return qt, st
 
 
-def requant_t_128x1(q, s):
+def requant_t_128x1(q, s, pow2_scales=False):
     """FP8 activation cache q uint8 [rows, cols] with chunk-major 1x128 scales s [cols/128, >=rows]
     -> (qt uint8 [cols, rows], st float32 [rows/128, cols]): 128x1 tiles with power-of-two scales,
-    the layout of COLWISE quantisation."""
+    the layout of COLWISE quantisation. pow2_scales: s holds powers of two (the kernel for that
+    case; the result is the same)."""
     import torch
     if q.dtype != torch.uint8 or q.dim() != 2 or q.stride(1) != 1:
         raise ValueError("q must be a 2-D row-major uint8 tensor")
@@ -272,7 +273,7 @@ def requant_t_128x1(q, s):
     qt = torch.empty((cols, rows), dtype=torch.uint8, device=q.device)
     st = torch.empty((rows // 128, cols), dtype=torch.float32, device=q.device)
     fp8bq_requant_t_128x1(q.data_ptr(), rows, cols, q.stride(0), s.data_ptr(), s.stride(0), qt.data_ptr(), rows,
-                          st.data_ptr(), cols, 0, _stream(q))
+                          st.data_ptr(), cols, SCALE_POW2 if pow2_scales else 0, _stream(q))
     return qt, st
 
 

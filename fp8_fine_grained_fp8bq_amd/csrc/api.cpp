@@ -165,7 +165,7 @@ int fp8bq_requant_e5m6_t_128x1(const void* q, int64_t rows, int64_t cols, int64_
 int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq, const float* s, int64_t lds,
                           void* qt, int64_t ldqt, float* st, int64_t ldst, int flags, void* stream) {
   if (!q || !s || !qt || !st) return fail(FP8BQ_E_INVAL, "requant_t: null pointer");
-  if (flags) return fail(FP8BQ_E_INVAL, "requant_t: flags must be 0, got %d", flags);
+  if (flags & ~FP8BQ_SCALE_POW2) return fail(FP8BQ_E_INVAL, "requant_t: unknown flags %d", flags);
   if (rows <= 0 || cols <= 0) return fail(FP8BQ_E_INVAL, "requant_t: rows and cols must be positive");
   if (ldq < cols || ldqt < rows) return fail(FP8BQ_E_INVAL, "requant_t: ldq must be >= cols and ldqt >= rows");
   if (lds < rows || ldst < cols) return fail(FP8BQ_E_INVAL, "requant_t: lds must be >= rows and ldst >= cols");
@@ -177,7 +177,7 @@ int fp8bq_requant_t_128x1(const void* q, int64_t rows, int64_t cols, int64_t ldq
   if (ldq % 16 || ldqt % 16) return fail(FP8BQ_E_ALIGN, "requant_t: ldq and ldqt must be multiples of 16");
   if (int stt = check_device()) return stt;
   return launched(fp8bq::launch_requant_t(static_cast<const uint8_t*>(q), rows, cols, ldq, s, lds,
-                                          static_cast<uint8_t*>(qt), ldqt, st, ldst,
+                                          static_cast<uint8_t*>(qt), ldqt, st, ldst, (flags & FP8BQ_SCALE_POW2) != 0,
                                           reinterpret_cast<hipStream_t>(stream)), "requant_t");
 }
 

@@ -17,8 +17,10 @@ hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, 
 hipError_t launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, uint8_t* q,
                           int64_t ldq, float* s, int64_t lds, uint8_t* qt, int64_t ldqt,
                           bool pow2, hipStream_t st);
+// pow2_hint: the caller's scales are powers of two (same result, faster kernel).
 hipError_t launch_requant_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
-                            int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream);
+                            int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, bool pow2_hint,
+                            hipStream_t stream);
 
 // E5M6 activation cache: bf16 [rows, cols] -> packed 12-bit codes (1.5 B per
 // element, ldq in bytes) + chunk-major power-of-two scales, and back to bf16.

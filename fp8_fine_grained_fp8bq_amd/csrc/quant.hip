@@ -251,6 +251,10 @@ __device__ __forceinline__ int pow2_exponent_f64(double a) {
   return max(-127, min(127, k));
 }
 
+// POW2_HINT: the caller's scales are powers of two (FP8BQ_SCALE_POW2): blocks
+// whose row scales all qualify take a binary32 path (below); the others, and
+// every block without the hint, the float64 path. The results are the same.
+template <bool POW2_HINT>
 __global__ __launch_bounds__(256) void requant_t_kernel(
     const uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ s, int64_t lds,
     uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
@@ -286,15 +290,7 @@ __global__ __launch_bounds__(256) void requant_t_kernel(
   // and x_hat * 2^-k (exact, or below 2^-126, where it encodes to a signed
   // zero whether rounded or flushed): the float64 path's values, at a fraction
   // of its cost. A wave takes this path when every lane's scales qualify.
-  bool fast = true;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t b = __float_as_uint(sf[i]);
-    fast = fast && (b & 0x807FFFFFu) == 0u && (b >> 23) - 10u <= 235u;   // exponent field 10 .. 245
-  }
-  // Output row b of the thread (column 4p + b) is byte b of every w[i]: it is
-  // formed and encoded four values at a time, so only w, sf and four codes are
-  // live (all 64 values at once would take most of the register file).
+  // Output row b of the thread (column 4p + b) is byte b of every w[i].
   auto emit = [&](int b, auto&& value) {
     uint4 o;
     uint32_t* const op = reinterpret_cast<uint32_t*>(&o);
@@ -303,13 +299,46 @@ __global__ __launch_bounds__(256) void requant_t_kernel(
       op[g] = cvt4(value(4 * g, b), value(4 * g + 1, b), value(4 * g + 2, b), value(4 * g + 3, b));
     *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldqt + r0 + seg * 16) = o;
   };
+  // reform(): tells the compiler that w may have changed, so that a pass forms
+  // its values again instead of keeping an earlier pass's live (and decoding
+  // shared by two branches is not hoisted above them)
+  auto reform = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(w[i]));
+  };
   auto dec1 = [&](int i, int b) {   // (b is a constant once unrolled: one conversion)
     const int x = (int)w[i];
     return b == 0 ? __builtin_amdgcn_cvt_f32_fp8(x, 0) : b == 1 ? __builtin_amdgcn_cvt_f32_fp8(x, 1)
          : b == 2 ? __builtin_amdgcn_cvt_f32_fp8(x, 2) : __builtin_amdgcn_cvt_f32_fp8(x, 3);
   };
+  // float64 path, pass 1: the column maxima of |x_hat|, exact
+  auto f64_max = [&](int (&k)[4]) {
+    double cmax[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float d[4];
+      dec4(w[i], d);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cmax[b] = fmax(cmax[b], fabs((double)d[b] * (double)sf[i]));
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) k[b] = pow2_exponent_f64(dmax_lane8(cmax[b]));
+  };
   int k[4];
-  if (__builtin_amdgcn_ballot_w64(!fast) == 0) {   // wave-uniform
+  bool fast = POW2_HINT;
+  if constexpr (POW2_HINT) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = __float_as_uint(sf[i]);
+      fast = fast && (b & 0x807FFFFFu) == 0u && (b >> 23) - 10u <= 235u;   // exponent field 10 .. 245
+    }
+    fast = __builtin_amdgcn_ballot_w64(!fast) == 0;   // wave-uniform
+  }
+  if (fast) {
+    // binary32 path: pass 2 forms x_hat again, output row by output row,
+    // encoding four values at a time (57 registers where keeping pass 1's
+    // values, or sharing them with the other branch, took 173-228)
+    reform();
     float cmax[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -319,27 +348,34 @@ __global__ __launch_bounds__(256) void requant_t_kernel(
       for (int b = 0; b < 4; ++b) cmax[b] = fmaxf(cmax[b], fabsf(d[b] * sf[i]));   // exact
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      k[b] = pow2_exponent_f32(__uint_as_float(lane8_max(__float_as_uint(cmax[b]))));
-      emit(b, [&](int i, int bb) { return ldexpf(dec1(i, bb) * sf[i], -k[bb]); });
-    }
+    for (int b = 0; b < 4; ++b) k[b] = pow2_exponent_f32(__uint_as_float(lane8_max(__float_as_uint(cmax[b]))));
+    reform();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) emit(b, [&](int i, int bb) { return ldexpf(dec1(i, bb) * sf[i], -k[bb]); });
+  } else if constexpr (POW2_HINT) {
+    // a hinted launch whose block has other scales: float64, forming x_hat
+    // again in pass 2 (keeping the registers of the binary32 path's kernel)
+    reform();
+    f64_max(k);
+    reform();
+#pragma unroll
+    for (int b = 0; b < 4; ++b)   // exact product, one rounding
+      emit(b, [&](int i, int bb) { return (float)ldexp((double)dec1(i, bb) * (double)sf[i], -k[bb]); });
   } else {
-    // pass 1: the column maxima of |x_hat|; pass 2 forms x_hat again (cheaper
-    // than keeping 64 float64 values live)
-    double cmax[4] = {0.0, 0.0, 0.0, 0.0};
+    // float64 path: pass 2 scales the products of pass 1, which the compiler
+    // keeps live (148-175 registers; forming them again is 13% slower, the
+    // path being bound by its float64 arithmetic)
+    f64_max(k);
+    float v[4][16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float d[4];
       dec4(w[i], d);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) cmax[b] = fmax(cmax[b], fabs((double)d[b] * (double)sf[i]));   // exact
+      for (int b = 0; b < 4; ++b) v[b][i] = (float)ldexp((double)d[b] * (double)sf[i], -k[b]);   // exact, one rounding
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      k[b] = pow2_exponent_f64(dmax_lane8(cmax[b]));
-      // exact product, one rounding
-      emit(b, [&](int i, int bb) { return (float)ldexp((double)dec1(i, bb) * (double)sf[i], -k[bb]); });
-    }
+    for (int b = 0; b < 4; ++b) emit(b, [&](int i, int bb) { return v[bb][i]; });
   }
   if (seg == 0) {
     float4 sc;
@@ -771,9 +807,13 @@ hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 hipError_t launch_requant_t(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* s,
-                            int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t stream) {
+                            int64_t lds, uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, bool pow2_hint,
+                            hipStream_t stream) {
   dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 128));
-  hipLaunchKernelGGL(requant_t_kernel, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
+  if (pow2_hint)
+    hipLaunchKernelGGL(requant_t_kernel<true>, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
+  else
+    hipLaunchKernelGGL(requant_t_kernel<false>, grid, dim3(256), 0, stream, q, ldq, s, lds, qt, ldqt, st, ldst);
   return hipGetLastError();
 }
 

@@ -189,9 +189,14 @@ int fp8bq_requant_e5m6_t_128x1(const void* q, int64_t rows, int64_t cols, int64_
  *       at st[c * ldst + j], ldst >= cols: 2^k with k the smallest integer
  *       such that the tile's absmax <= 448 * 2^k, within [-127, 127] (2^-127
  *       for an all-zero tile); codes are E4M3(fl32(x_hat * 2^-k)).
- * flags must be 0. rows and cols must be multiples of 128.
+ * flags 0, or FP8BQ_SCALE_POW2 when the scales in s are powers of two (as
+ *       fp8bq_quant_act_1x128 writes them with that flag): a kernel specialised
+ *       for that case, which forms x_hat in binary32 wherever that is exact.
+ *       The outputs are the same for either value (each 128-row block checks
+ *       its own scales), so the flag is only a hint.
+ * rows and cols must be multiples of 128.
  * The caller owns all buffers; q/s and qt/st must not overlap.
- * Errors: E_INVAL (null, sizes <= 0, ld too small, flags), E_SHAPE,
+ * Errors: E_INVAL (null, sizes <= 0, ld too small, unknown flags), E_SHAPE,
  *         E_ALIGN (q, qt 16-byte aligned; ldq, ldqt multiples of 16; scales
  *         4-byte aligned), E_DEVICE, E_HIP.
  */

@@ -51,7 +51,7 @@ hipError_t launch_quant_w(const uint16_t*, int64_t n, int64_t k, int64_t, uint8_
   return LAUNCHED();
 }
 hipError_t launch_requant_t(const uint8_t*, int64_t rows, int64_t cols, int64_t, const float*, int64_t, uint8_t*,
-                            int64_t, float*, int64_t, hipStream_t) {
+                            int64_t, float*, int64_t, bool, hipStream_t) {
   if (rows % 128 || cols % 128) std::abort();
   return LAUNCHED();
 }
@@ -295,6 +295,8 @@ static void accepted(int want) {
   EXPECT(fp8bq_quant_act_1x128(P(A16), 256, 1024, 1024, 1 | FP8BQ_SCALE_POW2, P(B16), 256, F(S4), 1024, nullptr), want);
   EXPECT(fp8bq_quant_w_128x128(P(A16), 256, 384, 384, P(B16), 384, F(S4), 3, nullptr, 0, 0, nullptr), want);
   EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, 0, nullptr), want);
+  EXPECT(fp8bq_requant_t_128x1(P(A16), 256, 384, 384, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, FP8BQ_SCALE_POW2,
+                               nullptr), want);
   EXPECT(fp8bq_cache_e5m6_1x128(P(A16), 100, 384, 384, P(B16), 576, F(S4), 100, nullptr), want);
   EXPECT(fp8bq_uncache_e5m6_1x128(P(B16), 100, 384, 576, F(S4), 100, P(A16), 384, nullptr), want);
   EXPECT(fp8bq_requant_e5m6_t_128x1(P(A16), 256, 384, 576, F(S4), 256, P(B16), 256, F(S4 + 4096), 384, nullptr), want);

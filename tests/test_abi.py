@@ -100,6 +100,8 @@ def test_requant_validation(L):
         return _st(L, f, *a)
     assert bad(0, None) == fb.E_INVAL
     assert bad(10, 1) == fb.E_INVAL and "flags" in L.fp8bq_last_error().decode()
+    assert bad(10, 1 | fb.SCALE_POW2) == fb.E_INVAL
+    assert bad(10, fb.SCALE_POW2) == fb.E_DEVICE                                # the power-of-two hint
     assert bad(1, 0) == fb.E_INVAL
     assert bad(1, 200) == fb.E_SHAPE
     assert bad(2, 300) == fb.E_SHAPE

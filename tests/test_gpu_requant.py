@@ -1,5 +1,6 @@
 """GPU parity of the transposing re-quantisation (1x128 FP8 cache -> 128x1 tiles
-with power-of-two scales), through the C ABI: codes and scales bit-exact against
+with power-of-two scales), through the C ABI, with flags 0 and with the
+power-of-two hint (both kernels, on every input): codes and scales bit-exact against
 `oracle.quant.requant_128x1` on the same inputs. Inputs are the oracle's own
 quantisation of seeded bf16 matrices (power-of-two and exact scales), uploaded
 in the C ABI's chunk-major scale layout.
@@ -16,7 +17,7 @@ from workloads import act
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_requant(q, s_nat, ldq=None, lds=None):
+def _gpu_requant(q, s_nat, ldq=None, lds=None, flags=0):
     """q uint8 [rows, cols], s_nat float32 [rows, cols/128] (oracle layout) -> GPU (qT, sT_nat)."""
     import torch
     rows, cols = q.shape
@@ -29,16 +30,19 @@ def _gpu_requant(q, s_nat, ldq=None, lds=None):
     qt = torch.full((cols, rows), 0xAA, dtype=torch.uint8, device="cuda")
     st = torch.full((rows // 128, cols), -1.0, dtype=torch.float32, device="cuda")
     fb.fp8bq_requant_t_128x1(qd.data_ptr(), rows, cols, ldq, sd.data_ptr(), lds, qt.data_ptr(), rows,
-                             st.data_ptr(), cols, 0, torch.cuda.current_stream().cuda_stream)
+                             st.data_ptr(), cols, flags, torch.cuda.current_stream().cuda_stream)
     return host(qt), np.ascontiguousarray(host(st).T)
 
 
 def _check(q, s, name, **kw):
-    log(f"[requant] {name}: {q.shape}")
-    qt, st = _gpu_requant(q, s, **kw)
+    # both kernels: flags 0 and the power-of-two hint, which must give the same
+    # result whatever the scales are
     eqt, est = quant.requant_128x1(q, s)
-    np.testing.assert_array_equal(st.view(np.uint32), est.view(np.uint32), err_msg=f"{name}: scales")
-    np.testing.assert_array_equal(qt, eqt, err_msg=f"{name}: codes")
+    for flags in (0, fb.SCALE_POW2):
+        log(f"[requant] {name}: {q.shape}, flags {flags:#x}")
+        qt, st = _gpu_requant(q, s, flags=flags, **kw)
+        np.testing.assert_array_equal(st.view(np.uint32), est.view(np.uint32), err_msg=f"{name}, flags {flags}: scales")
+        np.testing.assert_array_equal(qt, eqt, err_msg=f"{name}, flags {flags}: codes")
 
 
 @pytest.mark.parametrize("mode", ["pow2", "exact"])
@@ -122,9 +126,11 @@ def test_large_workload_sampled_blocks():
     for rb in blocks:
         qb, sb = quant.quant_act_1x128(cfg.x[rb * 128:(rb + 1) * 128], "pow2")
         q[rb * 128:(rb + 1) * 128], s[rb * 128:(rb + 1) * 128] = qb, sb
-    log(f"[requant] large {rows}x{cols}, blocks {blocks}")
-    qt, st = _gpu_requant(q, s)
-    for rb in blocks:
-        eqt, est = quant.requant_128x1(q[rb * 128:(rb + 1) * 128], s[rb * 128:(rb + 1) * 128])
-        np.testing.assert_array_equal(qt[:, rb * 128:(rb + 1) * 128], eqt)
-        np.testing.assert_array_equal(st[:, rb].view(np.uint32), est[:, 0].view(np.uint32))
+    expect = {rb: quant.requant_128x1(q[rb * 128:(rb + 1) * 128], s[rb * 128:(rb + 1) * 128]) for rb in blocks}
+    for flags in (0, fb.SCALE_POW2):
+        log(f"[requant] large {rows}x{cols}, blocks {blocks}, flags {flags:#x}")
+        qt, st = _gpu_requant(q, s, flags=flags)
+        for rb in blocks:
+            eqt, est = expect[rb]
+            np.testing.assert_array_equal(qt[:, rb * 128:(rb + 1) * 128], eqt)
+            np.testing.assert_array_equal(st[:, rb].view(np.uint32), est[:, 0].view(np.uint32))
