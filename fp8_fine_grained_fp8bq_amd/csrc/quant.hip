@@ -197,8 +197,8 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
 // lanes p takes four consecutive values within one unit and seg 0..7) then
 // touches 32 distinct dwords of one 128-byte stripe of banks, and a staging
 // store (8 lanes on one row) the 8 units of that row. (Rows padded to 33
-// dwords instead put rows 16 seg and 16 (seg + 4) on the same banks: a 2-way
-// conflict in every read.)
+// dwords instead put the rows 16 seg of four row groups on the same banks: a
+// 4-way conflict in every read.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int req_unit(int u, int r) { return u ^ ((r >> 4) & 7); }
 
