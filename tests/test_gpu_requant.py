@@ -59,6 +59,23 @@ def test_requant_matches_oracle(mode, rows, cols, seed, kw):
     _check(q, s, f"{mode} seed {seed}")
 
 
+def test_binding_with_and_without_hint():
+    # the Python binding, with and without the power-of-two hint, on a
+    # power-of-two cache (chunk-major scales as the quantiser writes them)
+    import torch
+    x = act(41, 256, 384)
+    q, s = quant.quant_act_1x128(x, "pow2")
+    eqt, est = quant.requant_128x1(q, s)
+    qd = dev(q)
+    sd = dev(np.ascontiguousarray(s.T))
+    for hint in (False, True):
+        qt, st = fb.requant_t_128x1(qd, sd, pow2_scales=hint)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(qt), eqt, err_msg=f"hint {hint}: codes")
+        np.testing.assert_array_equal(np.ascontiguousarray(host(st).T).view(np.uint32), est.view(np.uint32),
+                                      err_msg=f"hint {hint}: scales")
+
+
 def test_leading_dimensions_and_zero_blocks():
     x = act(36, 384, 256, outlier_p=0.005, outlier_mult=1000.0)
     q, s = quant.quant_act_1x128(x, "pow2")
