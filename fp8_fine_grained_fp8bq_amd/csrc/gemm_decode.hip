@@ -73,11 +73,6 @@ namespace {
 constexpr int kDN = 64;    // output columns of a full-K workgroup
 constexpr int kDN2 = 128;  // output columns of a half-K workgroup
 
-// LDS DMA of one dword per lane through a raw buffer resource (see dma16_buf).
-__device__ __forceinline__ void dma4_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
-}
 // dma16_buf with the non-temporal hint, for the weight stream: each weight byte
 // is read once per call, so it should not displace the activations (re-read by
 // every column slice) from the caches. With a clean cache the two cost the

@@ -132,6 +132,11 @@ __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(gbase), "s"(lds) : "memory", "m0");
 }
+// A 4-byte LDS DMA through a raw buffer resource (lane i's bytes to M0 + 4 i).
+__device__ __forceinline__ void dma4_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
 // The same 16-byte LDS DMA through a raw buffer resource (base, byte bound):
 // a lane whose offset (VGPR, no scalar offset, no thread-id addressing) is at
 // or past the bound reads nothing from memory and its bytes come back as
@@ -570,6 +575,17 @@ struct Loader {
     }
   }
 
+  // L2 prefetch of the cursor's step (8 waves): one 4-byte LDS DMA per lane, one
+  // lane per 128-byte line of the step's chunk, waves 0-3 the 256 activation
+  // rows, 4-7 the weight rows; the bytes land in a scratch area nobody reads.
+  // Issued right after advance(), it reaches L2 one step before that step's own
+  // loads, which then hit there.
+  __device__ __forceinline__ void prefetch(uint32_t junk) const {
+    static_assert(WAVES == 8, "prefetch rows: 8 waves");
+    if (wave < 4) dma4_buf(rs_a, (uint32_t)(wave * 64 + lane) * (uint32_t)p.lda, junk);
+    else dma4_buf(rs_b, (uint32_t)((wave - 4) * 64 + lane) * (uint32_t)p.ldb, junk);
+  }
+
   // Load instruction q of the cursor's step into stage st.
   __device__ __forceinline__ void part(int q, int st) const {
     const uint32_t base = smem_base + (uint32_t)(st * S::kStage);
@@ -611,6 +627,19 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
   using C = Cfg<WAVES_M, WAVES_N, TBN>;
   using S = Stage<TBN>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::kStage];
+  // Grouped (MoE) GEMMs prefetch each step's chunk into L2 one step ahead. Their
+  // activations come from HBM, and their steps take 3833 cycles against 3138 with
+  // no loads at all; the prefetch takes the MoE workload from 712-724 to 705-708 us
+  // (three rounds of each). The large fprop's and the backward GEMMs' operands sit
+  // in the MALL (their loads cost 2% of a step), and there the prefetch costs 2-4%.
+  // After each step's loads every wave issues exactly one prefetch, which the
+  // barrier's wait lets stay in flight (loads complete in issue order).
+#ifdef FP8BQ_PREFETCH_ALL
+  constexpr bool kPF = true;
+#else
+  constexpr bool kPF = GROUPED;
+#endif
+  __shared__ uint32_t pf_junk[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -680,6 +709,7 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
 #pragma unroll
   for (int q = 0; q < kParts; ++q) ld.part(q, 1);
   ld.advance();
+  if constexpr (kPF) ld.prefetch(lds_addr(pf_junk));
 
   // Weight fragments are read kBAhead columns before their MFMAs (one column
   // for WGRAD, whose column scales take the registers). The earlier the
@@ -758,7 +788,8 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         if (j == kBarCol) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (kPF) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");   // all but the prefetch
+          else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
           read_scales(nstage, scn, scn1, jbn, c + 1 < nc ? off_cur : off_nxt);
         }
@@ -800,7 +831,10 @@ __global__ __launch_bounds__((Cfg<WAVES_M, WAVES_N, TBN>::kThreads)) void gemm_k
               for (int q = 0; q < kParts; ++q)
                 if (q * kSlots / kParts == t - kFirst) ld.part(q, s & 1);
             }
-            if (t + 1 == kNT) ld.advance();
+            if (t + 1 == kNT) {
+              ld.advance();
+              if constexpr (kPF) ld.prefetch(lds_addr(pf_junk));
+            }
           }
           // keep this order: one MFMA, the fold of the result kLag MFMAs old,
           // then the reads due here (no result waits for the matrix core, and
