@@ -61,39 +61,50 @@ __device__ __forceinline__ uint2 encode8(const uint4 w, const TileScale& t) {
 // ---------------------------------------------------------------------------
 // 1x128 row-wise activation tiles.
 // One tile per aligned group of 8 lanes (each lane 16 bf16 = 32 B, stored as
-// 16 codes = 16 B). Grid: y = 128-column chunk, x = groups of 32 rows; the 8
-// tiles of a wave are 8 consecutive rows of one chunk, so every load
-// instruction reads 8 runs of 256 B and the wave's 8 scales land in 32
-// contiguous bytes of the chunk-major scale array.
+// 16 codes = 16 B), and each lane takes two neighbouring tiles of its row, both
+// loaded before any arithmetic. A 256-thread block covers 32 rows of two
+// column tiles: each load instruction reads 8 runs of 256 B, and a wave's 8
+// scales per tile land in 32 contiguous bytes of the chunk-major scale array.
+// Block b takes tile pair b % pairs of row group b / pairs: consecutive blocks
+// read neighbouring 512-byte pieces of the same rows (with one tile per block,
+// blocks walking along the rows were 12% faster on gfx950 than blocks walking
+// down a column of tiles). Two tiles per lane: 55.3-56.2 against 56.0-57.1 us
+// for one on X [16384, 7168] cold (rotated runs on one box); a layout whose load
+// instructions each read a 2 KB run of one row was slower still (57.7 us).
+// With an odd number of tiles per row, the last pair's second tile is its first.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
 constexpr int kRowsPerBlock = (kRowThreads / 64) * 8;
 
-// Block b takes column tile b % tpr of row group b / tpr: consecutive blocks
-// read neighbouring 256-byte pieces of the same rows (12% faster on gfx950 than
-// consecutive blocks walking down a column of tiles). Measured against a layout
-// whose load instructions each read a 2 KB run of one row (8 tiles; blocks of 32
-// rows writing whole 128-byte scale lines): 57.0 against 57.7 us on
-// X [16384, 7168] cold, interleaved runs on one box (53.8 us for the plain
-// read-2-bytes / write-1-byte stream).
 template <bool POW2>
 __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int rows, int tpr, uint8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
   const int lane = threadIdx.x & 63;
   const int l8 = lane & 7;
-  const int group = (int)(blockIdx.x / (unsigned)tpr);
-  const int col = (int)(blockIdx.x - (unsigned)group * (unsigned)tpr);
+  const int pairs = (tpr + 1) / 2;
+  const int group = (int)(blockIdx.x / (unsigned)pairs);
+  const int pc = (int)(blockIdx.x - (unsigned)group * (unsigned)pairs);
+  const int col0 = 2 * pc, col1 = min(2 * pc + 1, tpr - 1);
   const int r = group * kRowsPerBlock + (threadIdx.x >> 3);
   const int row = r < rows ? r : rows - 1;
-  const uint16_t* p = x + (int64_t)row * ldx + col * 128 + l8 * 16;
-  const uint4 v0 = *reinterpret_cast<const uint4*>(p);
-  const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
+  const uint16_t* p0 = x + (int64_t)row * ldx + col0 * 128 + l8 * 16;
+  const uint16_t* p1 = x + (int64_t)row * ldx + col1 * 128 + l8 * 16;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(p0);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(p0 + 8);
+  const uint4 w0 = *reinterpret_cast<const uint4*>(p1);
+  const uint4 w1 = *reinterpret_cast<const uint4*>(p1 + 8);
   const TileScale ts = group_scale<POW2>(lane8_max(mag_max16(v0, v1)));
+  const TileScale tt = group_scale<POW2>(lane8_max(mag_max16(w0, w1)));
   const uint2 a = encode8<POW2>(v0, ts), b = encode8<POW2>(v1, ts);
+  const uint2 c = encode8<POW2>(w0, tt), d = encode8<POW2>(w1, tt);
   if (r < rows) {
-    *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + col * 128 + l8 * 16) = make_uint4(a.x, a.y, b.x, b.y);
-    if (l8 == 0) s[(int64_t)col * lds + row] = ts.s;
+    *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + col0 * 128 + l8 * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    if (l8 == 0) s[(int64_t)col0 * lds + row] = ts.s;
+    if (col1 != col0) {
+      *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + col1 * 128 + l8 * 16) = make_uint4(c.x, c.y, d.x, d.y);
+      if (l8 == 0) s[(int64_t)col1 * lds + row] = tt.s;
+    }
   }
 }
 
@@ -788,7 +799,7 @@ __global__ __launch_bounds__(256) void requant_e5m6_t_kernel(
 hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st) {
   const int tpr = (int)(cols / 128);
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock * tpr));
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock * ((tpr + 1) / 2)));
   if (pow2)
     hipLaunchKernelGGL(quant_act_rows_kernel<true>, grid, dim3(kRowThreads), 0, st, x, ldx, (int)rows, tpr, q, ldq, s, lds);
   else
