@@ -69,8 +69,8 @@ __device__ __forceinline__ uint2 encode8(const uint4 w, const TileScale& t) {
 // read neighbouring 512-byte pieces of the same rows (with one tile per block,
 // blocks walking along the rows were 12% faster on gfx950 than blocks walking
 // down a column of tiles). Two tiles per lane: 55.3-56.2 against 56.0-57.1 us
-// for one on X [16384, 7168] cold (rotated runs on one box); a layout whose load
-// instructions each read a 2 KB run of one row was slower still (57.7 us).
+// for one on X [16384, 7168] cold (rotated runs on one box), four: 55.9-57.4; a
+// layout whose load instructions each read a 2 KB run of one row: 57.7 us.
 // With an odd number of tiles per row, the last pair's second tile is its first.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
