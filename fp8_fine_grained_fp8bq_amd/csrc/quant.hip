@@ -37,6 +37,21 @@ __device__ __forceinline__ uint32_t lane8_max(uint32_t v) {
   return v;
 }
 
+// Largest of v over lanes l and l ^ 16 (xor16_max) or l and l ^ 32
+// (xor32_max): gfx950's v_permlane16_swap_b32 exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second, v_permlane32_swap_b32 the
+// upper half of the first with the lower half of the second; with v as both
+// operands, the two results are v and its partner (one VALU instruction
+// instead of a round trip through the LDS crossbar).
+__device__ __forceinline__ uint32_t xor16_max(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return umax(a[0], a[1]);
+}
+__device__ __forceinline__ uint32_t xor32_max(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax(a[0], a[1]);
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Packed (two 16-bit lanes per dword) max of the bf16 magnitudes of 8 dwords;
@@ -429,8 +444,7 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   uint32_t m = umax(umax(mag_max16(v[0], v[1]), mag_max16(v[2], v[3])),
                     umax(mag_max16(v[4], v[5]), mag_max16(v[6], v[7])));
   m = row16_max(m);
-  m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
-  m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+  m = xor32_max(xor16_max(m));
   if ((t & 63) == 0) wmax[t >> 6] = m;
   __syncthreads();
   m = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(256) void quant_w2_kernel(
 #pragma unroll
   for (int i = 0; i < 16; i += 2) m = umax(m, mag_max16(v[i], v[i + 1]));
   m = row16_max(m);
-  m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+  m = xor32_max(m);
   if (lane == 0) wmax[wv][0] = m;
   if (lane == 16) wmax[wv][1] = m;
   __syncthreads();
