@@ -486,46 +486,52 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
 }
 
 // Weight blocks without the transposed copy: a workgroup quantises two
-// neighbouring 128x128 blocks along k, so each load instruction reads two rows
-// x 512 B (lane l: row 2 i + l / 32, columns 8 (l % 32) .. + 7, block (l / 16) % 2).
-// Absmax per block: DPP over each 16-lane row, lanes l and l ^ 32 (the two
-// rows), then the four waves through LDS. A k with an odd number of blocks
-// leaves the second block of the last workgroup empty: its lanes re-read the
-// first block and store nothing. Measured on W [18432, 7168] (cold, interleaved
-// runs on one box): 65.0 us against 65.8 us for one block per workgroup; the
-// plain read-2-bytes / write-1-byte stream takes 60.7 us.
+// neighbouring 128x128 blocks along k. Lane l takes 32 contiguous bytes (16
+// values) of one row: row 4 i + l / 16 of its wave's 32, block (l / 8) % 2,
+// columns 16 (l % 8) .. + 15; it stores 16 bytes of codes per row, so each
+// load and store instruction of a wave touches four rows of both blocks. Absmax per block: DPP
+// over each group of 8 lanes, lanes l ^ 16 and l ^ 32 (the other rows), then
+// the four waves through LDS. A k with an odd number of blocks leaves the
+// second block of the last workgroup empty: its lanes re-read the first block
+// and store nothing. Measured on W [18432, 7168] (interleaved runs on one box):
+// 64.3-65.0 us against 64.9-65.6 us for 16-byte loads and 8-byte stores per
+// lane, and 65.8 us for one block per workgroup; the plain read-2-bytes /
+// write-1-byte stream takes 60.7 us.
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_w2_kernel(
     const uint16_t* __restrict__ w, int64_t ldw, int kblocks, uint8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
   __shared__ uint32_t wmax[4][2];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int half = (lane >> 4) & 1;
+  const int rg = lane >> 4, half = (lane >> 3) & 1, l8 = lane & 7;
   const int kb = 2 * (int)blockIdx.x + half;
   const bool ok = kb < kblocks;
   const int64_t n0 = (int64_t)blockIdx.y * 128;
-  const int64_t col = (int64_t)(ok ? kb : kb - 1) * 128 + (lane & 15) * 8;
-  uint4 v[16];
+  const int64_t col = (int64_t)(ok ? kb : kb - 1) * 128 + l8 * 16;
+  uint4 v[8][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    v[i] = *reinterpret_cast<const uint4*>(w + (n0 + wv * 32 + 2 * i + (lane >> 5)) * ldw + col);
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t* pp = w + (n0 + wv * 32 + 4 * i + rg) * ldw + col;
+    v[i][0] = *reinterpret_cast<const uint4*>(pp);
+    v[i][1] = *reinterpret_cast<const uint4*>(pp + 8);
+  }
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) m = umax(m, mag_max16(v[i], v[i + 1]));
-  m = row16_max(m);
-  m = xor32_max(m);
+  for (int i = 0; i < 8; ++i) m = umax(m, mag_max16(v[i][0], v[i][1]));
+  m = xor32_max(xor16_max(lane8_max(m)));
   if (lane == 0) wmax[wv][0] = m;
-  if (lane == 16) wmax[wv][1] = m;
+  if (lane == 8) wmax[wv][1] = m;
   __syncthreads();
   m = umax(umax(wmax[0][half], wmax[1][half]), umax(wmax[2][half], wmax[3][half]));
   const TileScale ts = group_scale<POW2>(m);
   if (!ok) return;
-  if (t == 0 || t == 16) s[(int64_t)blockIdx.y * lds + kb] = ts.s;
+  if (t == 0 || t == 8) s[(int64_t)blockIdx.y * lds + kb] = ts.s;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    *reinterpret_cast<uint2*>(q + (n0 + wv * 32 + 2 * i + (lane >> 5)) * ldq + col) = encode8<POW2>(v[i], ts);
+  for (int i = 0; i < 8; ++i) {
+    const uint2 a = encode8<POW2>(v[i][0], ts), b = encode8<POW2>(v[i][1], ts);
+    *reinterpret_cast<uint4*>(q + (n0 + wv * 32 + 4 * i + rg) * ldq + col) = make_uint4(a.x, a.y, b.x, b.y);
+  }
 }
-
 
 // ---------------------------------------------------------------------------
 // E5M6 activation cache (report section 3.3.3, low-precision activations,
