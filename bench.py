@@ -124,7 +124,9 @@ def status_table(path):
     if "quant_act_128x1" in o:
         q = o["quant_act_128x1"]
         rows.append(("a5 128×1 token-direction quantisation, X [4096, 7168]", "quant_act_cols_kernel",
-                     f"{q['us']:.1f} µs cold, {q['GBps'] / 1000:.2f} TB/s = {pct(q['frac_hbm'])} of 8 TB/s"))
+                     f"{q['us']:.1f} µs cold, {q['GBps'] / 1000:.2f} TB/s = {pct(q['frac_hbm'])} of 8 TB/s"
+                     + (f", {pct(q['frac_ceiling'])} of the measured 2:1 streaming ceiling at this size"
+                        if q.get("frac_ceiling") else "")))
     for key, name, kern in (("dense_fprop", "a6–a8 Fprop GEMM, dense (4096×2048×7168)", "gemm_kernel<FPROP>, 256×128 tiles"),
                             ("dgrad", "a6–a8 Dgrad GEMM (4096×7168×2048)", "gemm_kernel<DGRAD>, 256×224 tiles"),
                             ("wgrad", "a6–a8 Wgrad GEMM (2048×7168×4096, fp32 out)", "gemm_kernel<WGRAD>, 256×224 tiles")):
@@ -827,6 +829,15 @@ def main():
         t_ow = st_t_ow["mean"]
         st_t_qc = time_kernel(o_qcol_x, args.kernel_reps, True)
         t_qc = st_t_qc["mean"]
+        # its ceiling at this size: the 2:1 stream over the same elements, cold
+        st_s_qc = None
+        if not args.no_probes:
+            from fp8_fine_grained_fp8bq_amd import probe
+
+            def o_stream_x():
+                probe.fp8bq_probe_stream_2to1(o_x.data_ptr(), o_xqt.data_ptr(), Md * Kd, sp)
+
+            st_s_qc = time_kernel(o_stream_x, args.kernel_reps, True)
         f_d = 2.0 * Md * Nd * Kd
         b_qc = Md * Kd * 3 + (Md // 128) * Kd * 4
         others["dense_fprop"] = {"what": f"GEMM {Md}x{Nd}x{Kd} (bf16 out)", "us": round(t_of, 2),
@@ -843,7 +854,9 @@ def main():
                            "us_stats": rnd(st_t_ow)}
         others["quant_act_128x1"] = {"what": f"token-direction (128x1) quantisation of X [{Md}, {Kd}], transposed out",
                                      "us": round(t_qc, 2), "GBps": round(b_qc / t_qc / 1e3, 1),
-                                     "frac_hbm": round(b_qc / t_qc / 1e3 / PEAK_HBM_GBS, 4), "us_stats": rnd(st_t_qc)}
+                                     "frac_hbm": round(b_qc / t_qc / 1e3 / PEAK_HBM_GBS, 4), "us_stats": rnd(st_t_qc),
+                                     "ceiling_us": round(st_s_qc["mean"], 2) if st_s_qc else None,
+                                     "frac_ceiling": round(st_s_qc["mean"] / t_qc, 4) if st_s_qc else None}
         del o_x, o_w, o_dy, o_y, o_dx, o_dw
         # MoE grouped fprop (8 local experts, Zipf top-8 routing, rows padded to 128)
         G_m, N_m, K_m = moe.w.shape
