@@ -125,21 +125,23 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // 128x1 column-wise tiles, written transposed.
-// A 256-thread block stages 128 rows x 128 columns of bf16 (32 KB) in LDS: 16
-// lanes per row load its 256 bytes, eight rows apart 16 at a time, so each
-// thread has eight 16-byte loads in flight. Thread t then owns columns
-// 4 (t / 8) .. + 3 and rows [16 (t % 8), +16): it reduces each column's absmax
-// with its 7 neighbours (one aligned group of 8 lanes), encodes its 16 rows of
-// each column and writes them as 16 contiguous bytes of the transposed output,
-// so every output row of the block is one full 128-byte line. (Blocks of 64
-// columns staged dword by dword ran at 64% of 8 TB/s on X [16384, 7168].)
+// A 256-thread block stages 128 rows x 64 columns of bf16 (16 KB) in LDS: 8
+// lanes per row load its 128 bytes, 32 rows at a time, so each thread has four
+// 16-byte loads in flight. Thread t then owns columns 2 (t / 8), 2 (t / 8) + 1
+// and rows [16 (t % 8), +16): it reduces each column's absmax with its 7
+// neighbours (one aligned group of 8 lanes), encodes its 16 rows of each column
+// and writes them as 16 contiguous bytes of the transposed output, so every
+// output row of the block is one full 128-byte line. Half-width blocks (16 KB
+// of LDS instead of 32) let 8 blocks share a CU instead of 5, which fills the
+// memory pipeline better through the launch's last blocks: on X [4096, 7168]
+// (interleaved runs on one box) 18.9-19.3 us against 19.8-19.9 us for 128
+// columns per block, with byte-identical output. (A first 64-column version
+// staged dword by dword ran at 64% of 8 TB/s on X [16384, 7168].)
 // LDS: the 16-byte unit u (columns 8u .. 8u + 7) of staged row r sits at unit
-// u ^ ((r / 16) % 8). The LDS serves 128 bytes per clock, 16 lanes of an
-// 8-byte read or 8 lanes of a 16-byte store at a time; a column read (16
-// lanes: 2 column quads of 8 rows 16 apart) then touches 16 distinct 8-byte
-// pieces of a 128-byte stripe, and a staging store (8 lanes on one row) 8
-// distinct units. (XOR by twice the row group, as first written, let row groups
-// g and g + 4 collide within 128 bytes: a 2-way conflict in every read.)
+// u ^ ((r / 16) % 8). The LDS serves 128 bytes per clock, 32 lanes of a 4-byte
+// read or 8 lanes of a 16-byte store at a time; a column read (32 lanes: 4
+// column pairs of one unit, 8 rows 16 apart) then touches 32 distinct banks,
+// and a staging store (8 lanes on one row) 8 distinct units.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int cols_swz(int r) { return (r >> 4) & 7; }
 
@@ -147,57 +149,46 @@ template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
     float* __restrict__ s, int64_t lds) {
-  __shared__ uint4 tile[128 * 16];   // 128 rows x 16 units of 16 bytes
+  __shared__ uint4 tile[128 * 8];   // 128 rows x 8 units of 16 bytes (64 columns)
   const int t = threadIdx.x;
-  // row blocks vary fastest: consecutive blocks write neighbouring 128-byte
-  // pieces of the same transposed rows
   const int64_t r0 = (int64_t)blockIdx.x * 128;
-  const int64_t c0 = (int64_t)blockIdx.y * 128;
-  const int l16 = t & 15, rs = t >> 4;
-
-  uint4 in[8];
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  const int l8 = t & 7, rs = t >> 3;
+  uint4 in[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    in[j] = *reinterpret_cast<const uint4*>(x + (r0 + 16 * j + rs) * ldx + c0 + l16 * 8);
+  for (int j = 0; j < 4; ++j)
+    in[j] = *reinterpret_cast<const uint4*>(x + (r0 + 32 * j + rs) * ldx + c0 + l8 * 8);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) tile[(16 * j + rs) * 16 + (l16 ^ cols_swz(16 * j))] = in[j];
+  for (int j = 0; j < 4; ++j) tile[(32 * j + rs) * 8 + (l8 ^ cols_swz(32 * j + rs))] = in[j];
   __syncthreads();
 
-  const int p = t >> 3, seg = t & 7;
-  const uint2* lt = reinterpret_cast<const uint2*>(tile);
-  uint2 w[16];
-  uint32_t m[4] = {0u, 0u, 0u, 0u};
+  const int p = t >> 3, seg = t & 7;   // columns 2p, 2p + 1; rows 16 seg .. + 15
+  const uint32_t* lt = reinterpret_cast<const uint32_t*>(tile);
+  uint32_t w[16];
+  uint32_t m0 = 0u, m1 = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = seg * 16 + i;
-    // columns 4p .. 4p + 3: half (p & 1) of logical unit p / 2, i.e. 8-byte
-    // piece 2 ((p / 2) ^ g) + (p & 1) = p ^ 2 g
-    w[i] = lt[row * 32 + (p ^ (2 * cols_swz(row)))];
-    m[0] = umax(m[0], w[i].x & 0x7FFFu);
-    m[1] = umax(m[1], (w[i].x >> 16) & 0x7FFFu);
-    m[2] = umax(m[2], w[i].y & 0x7FFFu);
-    m[3] = umax(m[3], (w[i].y >> 16) & 0x7FFFu);
+    w[i] = lt[row * 32 + (((p >> 2) ^ cols_swz(row)) << 2) + (p & 3)];
+    m0 = umax(m0, w[i] & 0x7FFFu);
+    m1 = umax(m1, (w[i] >> 16) & 0x7FFFu);
   }
-  TileScale ts[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) ts[b] = group_scale<POW2>(lane8_max(m[b]));
-
-  auto col_value = [&](int i, int b) {
-    return b == 0 ? bf_lo(w[i].x) : b == 1 ? bf_hi(w[i].x) : b == 2 ? bf_lo(w[i].y) : bf_hi(w[i].y);
-  };
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    uint4 o;
-    o.x = encode4<POW2>(col_value(0, b), col_value(1, b), col_value(2, b), col_value(3, b), ts[b]);
-    o.y = encode4<POW2>(col_value(4, b), col_value(5, b), col_value(6, b), col_value(7, b), ts[b]);
-    o.z = encode4<POW2>(col_value(8, b), col_value(9, b), col_value(10, b), col_value(11, b), ts[b]);
-    o.w = encode4<POW2>(col_value(12, b), col_value(13, b), col_value(14, b), col_value(15, b), ts[b]);
-    *reinterpret_cast<uint4*>(qt + (c0 + 4 * p + b) * ldq + r0 + seg * 16) = o;
-  }
+  const TileScale t0 = group_scale<POW2>(lane8_max(m0)), t1 = group_scale<POW2>(lane8_max(m1));
+  uint4 o0, o1;
+  o0.x = encode4<POW2>(bf_lo(w[0]), bf_lo(w[1]), bf_lo(w[2]), bf_lo(w[3]), t0);
+  o0.y = encode4<POW2>(bf_lo(w[4]), bf_lo(w[5]), bf_lo(w[6]), bf_lo(w[7]), t0);
+  o0.z = encode4<POW2>(bf_lo(w[8]), bf_lo(w[9]), bf_lo(w[10]), bf_lo(w[11]), t0);
+  o0.w = encode4<POW2>(bf_lo(w[12]), bf_lo(w[13]), bf_lo(w[14]), bf_lo(w[15]), t0);
+  o1.x = encode4<POW2>(bf_hi(w[0]), bf_hi(w[1]), bf_hi(w[2]), bf_hi(w[3]), t1);
+  o1.y = encode4<POW2>(bf_hi(w[4]), bf_hi(w[5]), bf_hi(w[6]), bf_hi(w[7]), t1);
+  o1.z = encode4<POW2>(bf_hi(w[8]), bf_hi(w[9]), bf_hi(w[10]), bf_hi(w[11]), t1);
+  o1.w = encode4<POW2>(bf_hi(w[12]), bf_hi(w[13]), bf_hi(w[14]), bf_hi(w[15]), t1);
+  *reinterpret_cast<uint4*>(qt + (c0 + 2 * p) * ldq + r0 + seg * 16) = o0;
+  *reinterpret_cast<uint4*>(qt + (c0 + 2 * p + 1) * ldq + r0 + seg * 16) = o1;
   if (seg == 0) {
-    float* sp = s + (int64_t)blockIdx.x * lds + c0 + 4 * p;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) sp[b] = ts[b].s;
+    float* sp = s + (int64_t)blockIdx.x * lds + c0 + 2 * p;
+    sp[0] = t0.s;
+    sp[1] = t1.s;
   }
 }
 
@@ -829,7 +820,7 @@ hipError_t launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 
 hipError_t launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* qt, int64_t ldq, float* s, int64_t lds, bool pow2, hipStream_t st) {
-  dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 128));
+  dim3 grid((unsigned)(rows / 128), (unsigned)(cols / 64));
   if (pow2)
     hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, st, x, ldx, qt, ldq, s, lds);
   else
