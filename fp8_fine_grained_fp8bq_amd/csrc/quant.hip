@@ -135,7 +135,8 @@ __global__ __launch_bounds__(kRowThreads) void quant_act_rows_kernel(
 // of LDS instead of 32) let 8 blocks share a CU instead of 5, which fills the
 // memory pipeline better through the launch's last blocks: on X [4096, 7168]
 // (interleaved runs on one box) 18.9-19.3 us against 19.8-19.9 us for 128
-// columns per block, with byte-identical output. (A first 64-column version
+// columns per block, with byte-identical output; on X [16384, 7168] 61.9-62.3
+// us against 62.8-63.2 us. (A first 64-column version
 // staged dword by dword ran at 64% of 8 TB/s on X [16384, 7168].)
 // LDS: the 16-byte unit u (columns 8u .. 8u + 7) of staged row r sits at unit
 // u ^ ((r / 16) % 8). The LDS serves 128 bytes per clock, 32 lanes of a 4-byte
